@@ -1,0 +1,266 @@
+"""Benchmark: paged decode attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4]
+
+A step is one pass of the whole path over one batch: for the default workload
+(16 layers, 256 sequences, lognormal contexts, 32q/8kv, d=64) that is, per
+layer, the paged append of the new token's K/V then paged decode attention
+(split kernel + merge kernel). Inputs are resident in HBM before timing.
+Prints one JSON line: achieved KV-read GB/s over the timed steps, the
+roofline of the dominant kernel (the decode split kernel, timed with HIP
+events on its own stream inside the timed region), and a CPU baseline (the
+FP64 oracle on a bounded sample of the same workload, on the host cores).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E peak
+MALL_BYTES = 256 << 20   # device last-level (Infinity) cache
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c4", choices=["tiny", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of timed oracle work for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
+    return ap.parse_args()
+
+
+class Inputs:
+    """One replica of a workload's device inputs."""
+
+    def __init__(self, w, dev, B):
+        import torch
+        self.k = w.pool_device("k", dev)
+        self.v = w.pool_device("v", dev)
+        self.pool = B.Pool(self.k, self.v)
+        self.bt = torch.from_numpy(np.ascontiguousarray(w.block_tables)).to(dev)
+        self.ctx = torch.from_numpy(w.ctx_lens).to(dev)
+        self.q = torch.from_numpy(w.q_bits().view(np.int16)).to(dev)
+        if w.append:
+            self.k_new = torch.from_numpy(w.new_kv_bits("k").view(np.int16)).to(dev)
+            self.v_new = torch.from_numpy(w.new_kv_bits("v").view(np.int16)).to(dev)
+            self.pos = torch.from_numpy(w.positions).to(dev)
+        need = B.decode_workspace_bytes(self.pool, w.num_seqs, w.num_q_heads, w.stride)
+        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((w.num_layers, w.num_seqs, w.num_q_heads, w.head_dim),
+                               dtype=torch.float32, device=dev)
+
+
+def run_step(w, x, B, stream):
+    for layer in range(w.num_layers):
+        if w.append:
+            B.kv_append(x.pool, x.k_new[layer], x.v_new[layer], x.bt[layer], x.pos, stream=stream)
+        B.decode(x.pool, x.q[layer], x.bt[layer], x.ctx, float(w.scale), out=x.out[layer],
+                 workspace=x.ws, stream=stream)
+
+
+def stream_ceiling(B, dev, stream):
+    import torch
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        B.stream_read(buf, sink, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    reps = 10
+    for _ in range(reps):
+        B.stream_read(buf, sink, stream=stream)
+    e1.record(stream)
+    e1.synchronize()
+    gbps = reps * buf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+    return gbps
+
+
+def cpu_baseline(w, budget_s):
+    """The FP64 oracle on (layer, sequence) units of the same workload until about
+    budget_s seconds of oracle time have run. Page regeneration is not timed."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    q = w.q_bits()
+    kn = w.new_kv_bits("k") if w.append else None
+    vn = w.new_kv_bits("v") if w.append else None
+    rng = np.random.default_rng(2024)
+    units = [(l, b) for l in range(w.num_layers) for b in range(w.num_seqs)]
+    order = rng.permutation(len(units))
+    t_oracle = 0.0
+    nbytes = 0
+    done = 0
+    for i in order:
+        layer, b = units[i]
+        n = int(w.ctx_lens[b])
+        pages = w.sequence_pages(layer, b)
+        kp = w.pool_pages_bits("k", pages)
+        vp = w.pool_pages_bits("v", pages)
+        bt = np.arange(pages.size, dtype=np.int32)[None, :]
+        t0 = time.perf_counter()
+        if w.append:
+            kp, vp = oracle.kv_append(kp, vp, kn[layer][b:b + 1], vn[layer][b:b + 1], bt,
+                                      np.array([n - 1], np.int32))
+        oracle.decode_attention(q[layer][b:b + 1], kp, vp, bt, np.array([n], np.int32), w.scale)
+        t_oracle += time.perf_counter() - t0
+        nbytes += n * w.num_kv_heads * w.head_dim * 4
+        done += 1
+        if t_oracle >= budget_s:
+            break
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    gbps = nbytes / t_oracle / 1e9
+    return {"value": round(gbps, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {len(units)} (layer, sequence) units, random order, "
+                      f"{nbytes / 1e6:.1f} MB of KV in {t_oracle:.1f} s of oracle time; "
+                      f"BLAS limited to 1 thread",
+            "us_per_step_extrapolated": round(t_oracle / nbytes * w.kv_bytes_per_step() * 1e6, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path runs on a "
+              f"single MI355X and has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_kv_decode_02_amd import binding as B
+    from paged_kv_decode_02_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    B.lib()
+    w = W.make_workload(args.workload)
+    stream = torch.cuda.Stream(device=dev)     # default priority
+
+    # Workloads whose pool fits the device cache rotate over replicas so that
+    # every timed step reads from HBM.
+    replicas = 1
+    if w.pool_bytes() * 2 < 2 * MALL_BYTES:
+        replicas = max(2, math.ceil(4 * MALL_BYTES / w.pool_bytes()))
+        replicas = min(replicas, 16)
+    t0 = time.time()
+    xs = [Inputs(w, dev, B) for _ in range(replicas)]
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    print(f"[bench] {w.name}: pool {w.pool_bytes() / 1e9:.2f} GB x {replicas} replica(s), "
+          f"inputs made in {gen_s:.1f} s", file=sys.stderr, flush=True)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            run_step(w, xs[i % replicas], B, stream)
+    torch.cuda.synchronize()
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    B.profile_start()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for i in range(args.steps):
+            run_step(w, xs[i % replicas], B, stream)
+        e1.record(stream)
+    e1.synchronize()
+    torch.cuda.synchronize()
+    prof = B.profile_stop()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+    kv_step = w.kv_bytes_per_step()
+    value = kv_step / (ms_step * 1e-3) / 1e9
+
+    dec_ms, dec_n = prof["decode"]
+    mer_ms, mer_n = prof["merge"]
+    app_ms, app_n = prof["append"]
+    dec_avg_ms = dec_ms / max(dec_n, 1)
+    achieved = w.kv_bytes_per_layer() / (dec_avg_ms * 1e-3) / 1e9
+    print(f"[bench] step {ms_step * 1e3:.1f} us; decode kernel avg {dec_avg_ms * 1e3:.1f} us x "
+          f"{dec_n}, merge {mer_ms / max(mer_n, 1) * 1e3:.1f} us x {mer_n}, append "
+          f"{app_ms / max(app_n, 1) * 1e3:.1f} us x {app_n}", file=sys.stderr, flush=True)
+
+    ceiling = None
+    if not args.no_ceiling:
+        ceiling = stream_ceiling(B, dev, stream)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    result = {
+        "metric": "paged decode attention: achieved KV-read GB/s (% of HBM peak) + us/step",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "us_per_step": round(ms_step * 1e3, 1),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": {"tiny": "tiny: 1 seq x ctx 128, 32q/8kv d64, 1 layer",
+                         "c2": "batch 8, ctx U[1,512], 32q/8kv d64, 1 layer",
+                         "c3": "batch 64, ctx U[256,2048], 32q/8kv d64, 1 layer",
+                         "c4": "full decode step: 16 layers x (append + decode), batch 256, "
+                               "ctx lognormal median 1024 clipped [16,8192], 32q/8kv d64",
+                         "c5": "batch 64, ctx U[4096,16384], 28q/4kv d128, 1 layer"}[w.name],
+            "global_batch": w.num_seqs,
+            "layers": w.num_layers,
+            "q_heads": w.num_q_heads,
+            "kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim,
+            "page_tokens": W.PAGE,
+            "mean_ctx": round(float(w.ctx_lens.mean()), 1),
+            "kv_bytes_per_step": kv_step,
+            "pool_pages": w.num_pages,
+            "replicas": replicas,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_split_kernel",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(dec_avg_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": w.kv_bytes_per_layer(),
+        },
+        "kernels_us_per_step": {
+            "decode_split": round(dec_ms / args.steps * 1e3, 1),
+            "merge": round(mer_ms / args.steps * 1e3, 1),
+            "append": round(app_ms / args.steps * 1e3, 1),
+        },
+        "stream_read_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
+        "frac_of_stream_ceiling": None if ceiling is None else round(value / ceiling, 4),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/*
+ * pakv.h - C ABI of libpakv: decode-step paged attention over a shared pool
+ * of BF16 KV pages, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (sources cited by page title and section):
+ *
+ *  - "Curso gratuito recorre la inferencia de LLM con videos, notas y un motor
+ *    funcional en C++" (news-factory.app), section "¿Cómo administra el motor
+ *    la memoria de la caché KV?": one shared pool of BF16 pages, each physical
+ *    page holding keys and values for 16 tokens; one block table per sequence
+ *    and layer; decode attention reads each sequence's cached pages in place,
+ *    with an FP32 online softmax, instead of gathering a contiguous prefix. A
+ *    request that cannot be served is rejected with an error, not a crash.
+ *  - comrad404.com review of the samir-vllm README, section "Что README
+ *    говорит о KV-кэше и пакетном декодировании": decode adds the new token's
+ *    keys and values to the request's pages.
+ *  - "Construye tu propio motor de inferencia LLM de alto rendimiento en C++ y
+ *    CUDA" (aibit.im), section "Atención de Consulta Agrupada (GQA)": several
+ *    query heads share one KV head, grouped contiguously (query head h reads
+ *    KV head h / (Hq / Hkv)); section "El truco de transposición de cuBLAS":
+ *    the K/V projection yields one row of Hkv * head_dim BF16 values per
+ *    sequence, which is the append input.
+ *
+ * For sequence b with n = context_lens[b] cached tokens and query head h,
+ * g = h / (Hq / Hkv):
+ *     s_t      = scale * sum_i q[b][h][i] * K(b, t)[g][i]      t = 0 .. n-1
+ *     out[b][h] = sum_t softmax(s)_t * V(b, t)[g]
+ * where token t of sequence b is slot t % 16 of physical page
+ * block_tables[b][t / 16]. n == 0 gives an all-zero output row.
+ *
+ * Memory layout (all device memory is owned by the caller; the library never
+ * allocates, frees or synchronises, and queues all work on the caller's
+ * stream):
+ *  - K pool: BF16 [num_pages][num_kv_heads][16][head_dim]
+ *            element (p, g, slot, i) at ((p * Hkv + g) * 16 + slot) * d + i
+ *  - V pool: BF16 [num_pages][num_kv_heads][head_dim][16]
+ *            element (p, g, slot, i) at ((p * Hkv + g) * d + i) * 16 + slot
+ *    One physical page id indexes both pools. The V pool keeps the 16 slots of
+ *    each dimension together so that a decode lane's 16-byte load is exactly
+ *    one matrix-core operand (8 consecutive tokens of one dimension).
+ *  - q: BF16 [num_seqs][num_q_heads][head_dim]
+ *  - out: FP32 [num_seqs][num_q_heads][head_dim]
+ *  - k_new, v_new: BF16 [num_seqs][num_kv_heads][head_dim]
+ *  - block_tables: int32 [num_seqs][max_pages_per_seq] (one layer's table)
+ *  - context_lens, positions: int32 [num_seqs]
+ * Alignment: the pools, q, k_new, v_new and the workspace must be 16-byte
+ * aligned (they are read with 16-byte loads); out and the int32 arrays need
+ * 4-byte alignment.
+ *
+ * Device-resident data is not read by the host. Preconditions on it: page ids
+ * in [0, num_pages); context_lens[b] in [0, max_pages_per_seq * 16]; the
+ * tokens a sequence attends over hold finite values. The kernels clamp page
+ * ids and context lengths into range so that a violation cannot read or write
+ * outside the pool, but the result for that sequence is then meaningless.
+ * Slots past context_lens[b] and pages no block table names may hold any bits
+ * (NaN included): they never contribute.
+ *
+ * Errors: every entry point returns a pa_status and never aborts; arguments
+ * are validated on the host before any work is queued. A launch failure
+ * reported by the HIP runtime gives PA_ERR_LAUNCH.
+ */
+#ifndef PAKV_H
+#define PAKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PA_ERR_INVALID = 2,     /* a count or size is out of range */
+  PA_ERR_UNSUPPORTED = 3, /* valid in principle, not built: head_dim, page size, group size */
+  PA_ERR_ALIGN = 4,       /* a device pointer is not aligned as documented below */
+  PA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than pa_decode_workspace_bytes */
+  PA_ERR_LAUNCH = 6       /* the HIP runtime reported an error when queueing a kernel */
+} pa_status;
+
+/* Opaque host-side description of one K/V page pool (no device memory). */
+typedef struct pa_pool pa_pool;
+
+/*
+ * Describe a caller-owned pool. k_pages / v_pages: device pointers laid out as
+ * above. page_size must be 16 (the page of the samir-vllm pool);
+ * head_dim must be 64 or 128; num_kv_heads >= 1; num_pages >= 1.
+ * On success *out receives a descriptor to release with pa_pool_destroy.
+ * No device work is queued.
+ */
+pa_status pa_pool_create(pa_pool** out, void* k_pages, void* v_pages,
+                         int32_t num_pages, int32_t page_size,
+                         int32_t num_kv_heads, int32_t head_dim);
+
+/* Release a descriptor (not the pool memory). NULL is ignored. */
+void pa_pool_destroy(pa_pool* pool);
+
+/*
+ * Paged write of each sequence's new token (decode adds the new token's K/V,
+ * samir-vllm README review): for every b with 0 <= positions[b] <
+ * max_pages_per_seq * 16, copies k_new[b] / v_new[b] bit for bit into slot
+ * positions[b] % 16 of page block_tables[b][positions[b] / 16] in the K and V
+ * pools. A negative position skips the sequence; so does a page id outside
+ * the pool. No other pool byte changes. Queued on `stream` (a hipStream_t;
+ * NULL is the default stream); a pa_decode queued after it on the same
+ * stream sees the new token. num_seqs == 0 queues nothing.
+ */
+pa_status pa_kv_append(const pa_pool* pool, const void* k_new, const void* v_new,
+                       int32_t num_seqs, const int32_t* block_tables,
+                       int32_t max_pages_per_seq, const int32_t* positions,
+                       void* stream);
+
+/*
+ * Bytes of workspace pa_decode needs for these sizes (0 when every possible
+ * context fits one split). Long contexts are cut into splits of a fixed
+ * number of tokens per head_dim (pa_split_tokens); each split's partial
+ * softmax state is kept in the workspace and merged by log-sum-exp.
+ * Returns 0 for a NULL pool or non-positive sizes.
+ */
+size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t max_pages_per_seq);
+
+/* Tokens per split for a head_dim (64 or 128), 0 otherwise. Fixed per
+ * head_dim, so a sequence's result never depends on the rest of the batch. */
+int32_t pa_split_tokens(int32_t head_dim);
+
+/*
+ * Decode-step paged attention for one layer: out[b][h] as defined above,
+ * FP32 accumulation and FP32 online softmax. q: BF16 queries; num_q_heads a
+ * multiple of the pool's num_kv_heads with at most 16 query heads per KV
+ * head; block_tables / context_lens: this layer's table and lengths;
+ * scale: softmax scale (finite). workspace: device memory of at least
+ * pa_decode_workspace_bytes(...) bytes (may be NULL when that is 0); its
+ * contents need no initialisation and are overwritten. Queued on `stream`.
+ * num_seqs == 0 queues nothing.
+ */
+pa_status pa_decode(const pa_pool* pool, const void* q, int32_t num_seqs,
+                    int32_t num_q_heads, const int32_t* block_tables,
+                    int32_t max_pages_per_seq, const int32_t* context_lens,
+                    float scale, float* out, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Human-readable text for a status code (static storage). */
+const char* pa_status_str(pa_status status);
+
+/*
+ * Measurement helpers (not part of the attention path).
+ *
+ * pa_profile_start: from now on, bracket every kernel the library queues
+ * with a pair of HIP events on the same stream. pa_profile_stop waits for
+ * those events, returns the summed milliseconds and launch counts per kernel
+ * kind (index 0: decode split kernel, 1: split merge kernel, 2: append
+ * kernel) in ms[3] / launches[3], and stops recording. Not thread-safe.
+ */
+pa_status pa_profile_start(void);
+pa_status pa_profile_stop(double* ms, int64_t* launches);
+
+/*
+ * Streaming-read ceiling: reads `bytes` (a multiple of 16) from src with
+ * 16-byte loads and writes nothing visible except, improbably, one word of
+ * `sink`. Used to measure the achievable HBM read bandwidth of the device.
+ */
+pa_status pa_stream_read(const void* src, size_t bytes, void* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAKV_H */

@@ -1,0 +1,196 @@
+"""Thin Python binding of libpakv (ctypes). Argument marshalling only: every
+step of the attention path runs in the library's HIP kernels.
+
+Tensors are torch tensors on the GPU; BF16 data may be ``torch.bfloat16`` or
+``torch.int16`` bit patterns. Work is queued on torch's current stream unless
+a stream is given. The library never allocates device memory, so outputs and
+the decode workspace are allocated here with torch when not supplied.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpakv.so")
+
+PA_OK = 0
+STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_INVALID", 3: "PA_ERR_UNSUPPORTED",
+                4: "PA_ERR_ALIGN", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_LAUNCH"}
+EXPORTS = ["pa_pool_create", "pa_pool_destroy", "pa_kv_append", "pa_decode_workspace_bytes",
+           "pa_split_tokens", "pa_decode", "pa_status_str", "pa_profile_start",
+           "pa_profile_stop", "pa_stream_read"]
+
+_lib = None
+
+
+class PakvError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)} ({status_str(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpakv.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run python -m paged_kv_decode_02_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    c = ctypes
+    L.pa_pool_create.argtypes = [c.POINTER(c.c_void_p), c.c_void_p, c.c_void_p, c.c_int32,
+                                 c.c_int32, c.c_int32, c.c_int32]
+    L.pa_pool_create.restype = c.c_int
+    L.pa_pool_destroy.argtypes = [c.c_void_p]
+    L.pa_pool_destroy.restype = None
+    L.pa_kv_append.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_int32, c.c_void_p,
+                               c.c_int32, c.c_void_p, c.c_void_p]
+    L.pa_kv_append.restype = c.c_int
+    L.pa_decode_workspace_bytes.argtypes = [c.c_void_p, c.c_int32, c.c_int32, c.c_int32]
+    L.pa_decode_workspace_bytes.restype = c.c_size_t
+    L.pa_split_tokens.argtypes = [c.c_int32]
+    L.pa_split_tokens.restype = c.c_int32
+    L.pa_decode.argtypes = [c.c_void_p, c.c_void_p, c.c_int32, c.c_int32, c.c_void_p, c.c_int32,
+                            c.c_void_p, c.c_float, c.c_void_p, c.c_void_p, c.c_size_t, c.c_void_p]
+    L.pa_decode.restype = c.c_int
+    L.pa_status_str.argtypes = [c.c_int]
+    L.pa_status_str.restype = c.c_char_p
+    L.pa_profile_start.argtypes = []
+    L.pa_profile_start.restype = c.c_int
+    L.pa_profile_stop.argtypes = [c.POINTER(c.c_double), c.POINTER(c.c_int64)]
+    L.pa_profile_stop.restype = c.c_int
+    L.pa_stream_read.argtypes = [c.c_void_p, c.c_size_t, c.c_void_p, c.c_void_p]
+    L.pa_stream_read.restype = c.c_int
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().pa_status_str(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != PA_OK:
+        raise PakvError(status, what)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t, name, dtypes, ndim=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
+
+
+def _bf16_types():
+    import torch
+    return (torch.bfloat16, torch.int16)
+
+
+class Pool:
+    """A caller-owned K/V page pool: K ``[P][Hkv][16][d]``, V ``[P][Hkv][d][16]``."""
+
+    def __init__(self, k_pages, v_pages):
+        _need(k_pages, "k_pages", _bf16_types(), 4)
+        _need(v_pages, "v_pages", _bf16_types(), 4)
+        num_pages, hkv, page, d = k_pages.shape
+        if tuple(v_pages.shape) != (num_pages, hkv, d, page):
+            raise ValueError(f"v_pages shape {tuple(v_pages.shape)} does not match K {tuple(k_pages.shape)}")
+        handle = ctypes.c_void_p()
+        _check(lib().pa_pool_create(ctypes.byref(handle), _ptr(k_pages), _ptr(v_pages), num_pages,
+                                    page, hkv, d), "pa_pool_create")
+        self.handle = handle
+        self.k_pages, self.v_pages = k_pages, v_pages
+        self.num_pages, self.num_kv_heads, self.page_size, self.head_dim = num_pages, hkv, page, d
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            lib().pa_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def split_tokens(head_dim: int) -> int:
+    return int(lib().pa_split_tokens(head_dim))
+
+
+def decode_workspace_bytes(pool: Pool, num_seqs: int, num_q_heads: int, max_pages_per_seq: int) -> int:
+    return int(lib().pa_decode_workspace_bytes(pool.handle, num_seqs, num_q_heads, max_pages_per_seq))
+
+
+def kv_append(pool: Pool, k_new, v_new, block_tables, positions, stream=None):
+    """Write the new token's K/V (``[B][Hkv][d]``) at ``positions`` (pa_kv_append)."""
+    import torch
+    _need(k_new, "k_new", _bf16_types(), 3)
+    _need(v_new, "v_new", _bf16_types(), 3)
+    _need(block_tables, "block_tables", (torch.int32,), 2)
+    _need(positions, "positions", (torch.int32,), 1)
+    num_seqs = block_tables.shape[0]
+    _check(lib().pa_kv_append(pool.handle, _ptr(k_new), _ptr(v_new), num_seqs, _ptr(block_tables),
+                              block_tables.shape[1], _ptr(positions), _stream(stream)),
+           "pa_kv_append")
+
+
+def decode(pool: Pool, q, block_tables, context_lens, scale: float, out=None, workspace=None,
+           stream=None):
+    """Paged decode attention (pa_decode). Returns ``out`` (FP32 ``[B][Hq][d]``)."""
+    import torch
+    _need(q, "q", _bf16_types(), 3)
+    _need(block_tables, "block_tables", (torch.int32,), 2)
+    _need(context_lens, "context_lens", (torch.int32,), 1)
+    num_seqs, num_q_heads, d = q.shape
+    stride = block_tables.shape[1]
+    if out is None:
+        out = torch.empty((num_seqs, num_q_heads, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,), 3)
+    need = decode_workspace_bytes(pool, num_seqs, num_q_heads, stride)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode(pool.handle, _ptr(q), num_seqs, num_q_heads, _ptr(block_tables), stride,
+                           _ptr(context_lens), float(scale), _ptr(out), _ptr(workspace), ws_bytes,
+                           _stream(stream)), "pa_decode")
+    return out
+
+
+def profile_start():
+    _check(lib().pa_profile_start(), "pa_profile_start")
+
+
+def profile_stop():
+    """Returns {"decode": (ms, launches), "merge": (...), "append": (...)}."""
+    ms = (ctypes.c_double * 3)()
+    n = (ctypes.c_int64 * 3)()
+    _check(lib().pa_profile_stop(ms, n), "pa_profile_stop")
+    return {"decode": (ms[0], n[0]), "merge": (ms[1], n[1]), "append": (ms[2], n[2])}
+
+
+def stream_read(src, sink, stream=None):
+    """Read all of ``src`` with 16-byte loads (bandwidth ceiling measurement)."""
+    nbytes = src.numel() * src.element_size()
+    _check(lib().pa_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "pa_stream_read")

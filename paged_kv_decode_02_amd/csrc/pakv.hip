@@ -1,0 +1,315 @@
+// pakv.hip - host side of libpakv: argument validation, pool descriptor,
+// split/workspace sizing and kernel launches on the caller's stream.
+// The C ABI and the memory layout are documented in include/pakv.h.
+#include "pakv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <new>
+#include <vector>
+
+#include "pakv_kernels.h"
+
+// Split geometry per head_dim: pages per split and wavefronts per workgroup.
+// Fixed per head_dim so that a sequence's result does not depend on the batch.
+#ifndef PAKV_SPLIT_PAGES_D64
+#define PAKV_SPLIT_PAGES_D64 32
+#endif
+#ifndef PAKV_WAVES_D64
+#define PAKV_WAVES_D64 4
+#endif
+#ifndef PAKV_SPLIT_PAGES_D128
+#define PAKV_SPLIT_PAGES_D128 32
+#endif
+#ifndef PAKV_WAVES_D128
+#define PAKV_WAVES_D128 4
+#endif
+
+struct pa_pool {
+  void* k;
+  void* v;
+  int32_t num_pages;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+};
+
+namespace {
+
+constexpr int kMaxGroup = 16;   // query heads per KV head: the 16 MFMA columns
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int split_pages(int d) { return d == 64 ? PAKV_SPLIT_PAGES_D64 : PAKV_SPLIT_PAGES_D128; }
+int waves(int d) { return d == 64 ? PAKV_WAVES_D64 : PAKV_WAVES_D128; }
+
+int64_t splits_for(int d, int32_t max_pages_per_seq) {
+  const int64_t sp = split_pages(d);
+  return (static_cast<int64_t>(max_pages_per_seq) + sp - 1) / sp;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace: partial accumulators [B][Hq][S][D] then (m, l) pairs [B][Hq][S][2].
+void workspace_parts(int d, int32_t num_seqs, int32_t num_q_heads, int32_t max_pages_per_seq,
+                     size_t* acc_bytes, size_t* total) {
+  const int64_t s = splits_for(d, max_pages_per_seq);
+  if (s <= 1) {
+    *acc_bytes = 0;
+    *total = 0;
+    return;
+  }
+  const size_t items = static_cast<size_t>(num_seqs) * num_q_heads * s;
+  *acc_bytes = align_up(items * d * sizeof(float), 256);
+  *total = *acc_bytes + align_up(items * 2 * sizeof(float), 256);
+}
+
+// ---- optional event timing of each launch (measurement only)
+struct ProfileRec {
+  hipEvent_t start, stop;
+  int kind;
+};
+bool g_profiling = false;
+std::vector<ProfileRec> g_records;
+std::vector<hipEvent_t> g_free_events;
+
+hipEvent_t take_event() {
+  if (!g_free_events.empty()) {
+    hipEvent_t e = g_free_events.back();
+    g_free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct LaunchTimer {
+  ProfileRec rec{nullptr, nullptr, 0};
+  hipStream_t stream;
+  LaunchTimer(int kind, hipStream_t s) : stream(s) {
+    if (!g_profiling) return;
+    rec.kind = kind;
+    rec.start = take_event();
+    rec.stop = take_event();
+    if (rec.start) (void)hipEventRecord(rec.start, stream);
+  }
+  ~LaunchTimer() {
+    if (!g_profiling || !rec.start || !rec.stop) return;
+    (void)hipEventRecord(rec.stop, stream);
+    g_records.push_back(rec);
+  }
+};
+
+template <int D, int W, int SP>
+pa_status launch_decode(const pakv::DecodeArgs& args, hipStream_t stream) {
+  const int64_t blocks = static_cast<int64_t>(args.num_kv_heads) * args.num_seqs * args.s_max;
+  if (blocks > INT_MAX) return PA_ERR_INVALID;
+  const size_t lds = (2 * W * 16 + static_cast<size_t>(W) * args.group * (D + 4)) * sizeof(float);
+  (void)hipGetLastError();
+  {
+    LaunchTimer t(0, stream);
+    hipLaunchKernelGGL((pakv::decode_split_kernel<D, W, SP>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(64 * W), lds, stream, args);
+  }
+  if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
+  if (args.s_max > 1) {
+    const int64_t items = static_cast<int64_t>(args.num_seqs) * args.num_q_heads;
+    const int64_t mblocks = (items + 3) / 4;
+    if (mblocks > INT_MAX) return PA_ERR_INVALID;
+    {
+      LaunchTimer t(1, stream);
+      hipLaunchKernelGGL((pakv::merge_splits_kernel<D>), dim3(static_cast<unsigned>(mblocks)), dim3(256),
+                         0, stream, args, SP * pakv::kPage);
+    }
+    if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_str(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_INVALID: return "a count or size is out of range";
+    case PA_ERR_UNSUPPORTED: return "unsupported page size, head_dim or query-head group size";
+    case PA_ERR_ALIGN: return "a device pointer is not aligned as documented";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_LAUNCH: return "the HIP runtime failed to queue a kernel";
+  }
+  return "unknown status";
+}
+
+pa_status pa_pool_create(pa_pool** out, void* k_pages, void* v_pages, int32_t num_pages,
+                         int32_t page_size, int32_t num_kv_heads, int32_t head_dim) {
+  if (!out) return PA_ERR_NULL;
+  *out = nullptr;
+  if (!k_pages || !v_pages) return PA_ERR_NULL;
+  if (num_pages < 1 || num_kv_heads < 1 || page_size < 1 || head_dim < 1) return PA_ERR_INVALID;
+  if (page_size != pakv::kPage) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (!aligned16(k_pages) || !aligned16(v_pages)) return PA_ERR_ALIGN;
+  pa_pool* p = new (std::nothrow) pa_pool;
+  if (!p) return PA_ERR_INVALID;
+  p->k = k_pages;
+  p->v = v_pages;
+  p->num_pages = num_pages;
+  p->num_kv_heads = num_kv_heads;
+  p->head_dim = head_dim;
+  *out = p;
+  return PA_OK;
+}
+
+void pa_pool_destroy(pa_pool* pool) { delete pool; }
+
+int32_t pa_split_tokens(int32_t head_dim) {
+  if (head_dim != 64 && head_dim != 128) return 0;
+  return split_pages(head_dim) * pakv::kPage;
+}
+
+size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_pages_per_seq) {
+  if (!pool || num_seqs <= 0 || num_q_heads <= 0 || max_pages_per_seq <= 0) return 0;
+  size_t acc = 0, total = 0;
+  workspace_parts(pool->head_dim, num_seqs, num_q_heads, max_pages_per_seq, &acc, &total);
+  return total;
+}
+
+pa_status pa_kv_append(const pa_pool* pool, const void* k_new, const void* v_new, int32_t num_seqs,
+                       const int32_t* block_tables, int32_t max_pages_per_seq,
+                       const int32_t* positions, void* stream) {
+  if (!pool) return PA_ERR_NULL;
+  if (num_seqs < 0 || max_pages_per_seq < 1) return PA_ERR_INVALID;
+  if (static_cast<int64_t>(max_pages_per_seq) * pakv::kPage > INT_MAX) return PA_ERR_INVALID;
+  if (num_seqs == 0) return PA_OK;
+  if (!k_new || !v_new || !block_tables || !positions) return PA_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned4(block_tables) || !aligned4(positions))
+    return PA_ERR_ALIGN;
+  pakv::AppendArgs a;
+  a.kpool = static_cast<uint16_t*>(pool->k);
+  a.vpool = static_cast<uint16_t*>(pool->v);
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.block_tables = block_tables;
+  a.positions = positions;
+  a.num_pages = pool->num_pages;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.stride = max_pages_per_seq;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const unsigned blocks = static_cast<unsigned>((num_seqs + 3) / 4);
+  (void)hipGetLastError();
+  {
+    LaunchTimer t(2, s);
+    if (pool->head_dim == 64)
+      hipLaunchKernelGGL((pakv::kv_append_kernel<64>), dim3(blocks), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((pakv::kv_append_kernel<128>), dim3(blocks), dim3(256), 0, s, a);
+  }
+  if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+pa_status pa_decode(const pa_pool* pool, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                    const int32_t* block_tables, int32_t max_pages_per_seq,
+                    const int32_t* context_lens, float scale, float* out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (!pool) return PA_ERR_NULL;
+  if (num_seqs < 0 || num_q_heads < 1 || max_pages_per_seq < 1) return PA_ERR_INVALID;
+  if (static_cast<int64_t>(max_pages_per_seq) * pakv::kPage > INT_MAX) return PA_ERR_INVALID;
+  if (!std::isfinite(scale)) return PA_ERR_INVALID;
+  if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_INVALID;
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (group > kMaxGroup) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !block_tables || !context_lens || !out) return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned4(block_tables) || !aligned4(context_lens) || !aligned4(out))
+    return PA_ERR_ALIGN;
+  const int d = pool->head_dim;
+  size_t acc_bytes = 0, need = 0;
+  workspace_parts(d, num_seqs, num_q_heads, max_pages_per_seq, &acc_bytes, &need);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PA_ERR_ALIGN;
+  }
+  pakv::DecodeArgs a;
+  a.kpool = static_cast<const uint16_t*>(pool->k);
+  a.vpool = static_cast<const uint16_t*>(pool->v);
+  a.q = static_cast<const uint16_t*>(q);
+  a.block_tables = block_tables;
+  a.ctx = context_lens;
+  a.out = out;
+  a.ws_acc = need ? static_cast<float*>(workspace) : nullptr;
+  a.ws_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + acc_bytes) : nullptr;
+  a.num_pages = pool->num_pages;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.group = group;
+  a.stride = max_pages_per_seq;
+  a.s_max = static_cast<int32_t>(splits_for(d, max_pages_per_seq));
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d == 64) return launch_decode<64, PAKV_WAVES_D64, PAKV_SPLIT_PAGES_D64>(a, s);
+  return launch_decode<128, PAKV_WAVES_D128, PAKV_SPLIT_PAGES_D128>(a, s);
+}
+
+pa_status pa_profile_start(void) {
+  for (auto& r : g_records) {
+    g_free_events.push_back(r.start);
+    g_free_events.push_back(r.stop);
+  }
+  g_records.clear();
+  g_profiling = true;
+  return PA_OK;
+}
+
+pa_status pa_profile_stop(double* ms, int64_t* launches) {
+  if (!ms || !launches) return PA_ERR_NULL;
+  g_profiling = false;
+  for (int k = 0; k < 3; ++k) {
+    ms[k] = 0.0;
+    launches[k] = 0;
+  }
+  pa_status st = PA_OK;
+  for (auto& r : g_records) {
+    if (hipEventSynchronize(r.stop) != hipSuccess) {
+      st = PA_ERR_LAUNCH;
+      continue;
+    }
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess) {
+      st = PA_ERR_LAUNCH;
+      continue;
+    }
+    ms[r.kind] += t;
+    launches[r.kind] += 1;
+  }
+  for (auto& r : g_records) {
+    g_free_events.push_back(r.start);
+    g_free_events.push_back(r.stop);
+  }
+  g_records.clear();
+  return st;
+}
+
+pa_status pa_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!src || !sink) return PA_ERR_NULL;
+  if (bytes == 0 || bytes % 16 != 0) return PA_ERR_INVALID;
+  if (!aligned16(src) || !aligned16(sink)) return PA_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(pakv::stream_read_kernel, dim3(16384), dim3(256), 0, s,
+                     static_cast<const pakv::u32x4*>(src), bytes / 16, static_cast<uint32_t*>(sink));
+  if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+"""Shared helpers for the GPU tests: upload a workload, run the library through
+its C ABI (the ctypes binding), and compare with the oracle.
+
+Parity bar for decode (FP32 output vs the FP64 oracle): every element within
+2e-3 absolute, and within 1e-2 relative wherever |reference| >= 1e-2 (below
+that floor the absolute bound governs). The append is compared bit for bit.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+from paged_kv_decode_02_amd import binding as B
+
+ABS_TOL = 2e-3
+REL_TOL = 1e-2
+REL_FLOOR = 1e-2
+
+
+def log(msg: str):
+    print(f"[gpu-test] {msg}", file=sys.stderr, flush=True)
+
+
+def device():
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a ROCm GPU (torch.cuda.is_available() is False)")
+    return torch.device("cuda:0")
+
+
+def check_parity(gpu, ref, what: str):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, f"{what}: shape {gpu.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU output"
+    err = np.abs(gpu - ref)
+    max_abs = float(err.max()) if err.size else 0.0
+    big = np.abs(ref) >= REL_FLOOR
+    max_rel = float((err[big] / np.abs(ref[big])).max()) if np.any(big) else 0.0
+    assert max_abs <= ABS_TOL, f"{what}: max abs err {max_abs:.3e} > {ABS_TOL}"
+    assert max_rel <= REL_TOL, f"{what}: max rel err {max_rel:.3e} > {REL_TOL}"
+    return max_abs, max_rel
+
+
+class Uploaded:
+    """A workload's inputs resident on the GPU."""
+
+    def __init__(self, w, dev):
+        import torch
+        self.w = w
+        self.dev = dev
+        self.k_pool = w.pool_device("k", dev)
+        self.v_pool = w.pool_device("v", dev)
+        self.pool = B.Pool(self.k_pool, self.v_pool)
+        self.bt = torch.from_numpy(np.ascontiguousarray(w.block_tables)).to(dev)
+        self.ctx = torch.from_numpy(w.ctx_lens).to(dev)
+        self.q_host = w.q_bits()
+        self.q = torch.from_numpy(self.q_host.view(np.int16)).to(dev)
+        self.k_new_host = self.v_new_host = None
+        if w.append:
+            self.k_new_host = w.new_kv_bits("k")
+            self.v_new_host = w.new_kv_bits("v")
+            self.k_new = torch.from_numpy(self.k_new_host.view(np.int16)).to(dev)
+            self.v_new = torch.from_numpy(self.v_new_host.view(np.int16)).to(dev)
+            self.pos = torch.from_numpy(w.positions).to(dev)
+        stride = w.stride
+        need = B.decode_workspace_bytes(self.pool, w.num_seqs, w.num_q_heads, stride)
+        self.workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((w.num_layers, w.num_seqs, w.num_q_heads, w.head_dim),
+                               dtype=torch.float32, device=dev)
+
+    def step(self, layers=None):
+        """One decode step: per layer, append (when the workload appends) then decode."""
+        w = self.w
+        for layer in (range(w.num_layers) if layers is None else layers):
+            if w.append:
+                B.kv_append(self.pool, self.k_new[layer], self.v_new[layer], self.bt[layer], self.pos)
+            B.decode(self.pool, self.q[layer], self.bt[layer], self.ctx, float(w.scale),
+                     out=self.out[layer], workspace=self.workspace)
+        return self.out
+
+
+def oracle_rows(w, layer, seqs, q_host, k_new_host=None, v_new_host=None):
+    """Oracle outputs for the listed sequences of one layer, from host-regenerated
+    pages (only the pages those sequences reference)."""
+    outs = []
+    for b in seqs:
+        n = int(w.ctx_lens[b])
+        pages = w.sequence_pages(layer, b)
+        if n == 0:
+            outs.append(np.zeros((w.num_q_heads, w.head_dim)))
+            continue
+        kp = w.pool_pages_bits("k", pages)
+        vp = w.pool_pages_bits("v", pages)
+        bt = np.arange(pages.size, dtype=np.int32)[None, :]
+        if w.append:
+            kp, vp = oracle.kv_append(kp, vp, k_new_host[layer][b:b + 1], v_new_host[layer][b:b + 1],
+                                      bt, np.array([n - 1], np.int32))
+        o = oracle.decode_attention(q_host[layer][b:b + 1], kp, vp, bt, np.array([n], np.int32),
+                                    w.scale)
+        outs.append(o[0])
+    return np.stack(outs)

@@ -1,0 +1,180 @@
+"""GPU properties of the HIP path that hold at any size: bitwise determinism,
+batch invariance, placement invariance, shared pages, exact one-token output,
+bit-exact append that touches nothing else, the generator on the GPU, and the
+error paths of the C ABI."""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import Uploaded, check_parity, device, log
+from paged_kv_decode_02_amd import binding as B
+from paged_kv_decode_02_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def test_generator_on_gpu_matches_host():
+    import torch
+    dev = device()
+    w = W.custom(seed=2, ctx_lens=[5, 40, 100], num_q_heads=28, num_kv_heads=4, head_dim=128)
+    log("generator k/v pools on cuda:0 vs host")
+    for which in "kv":
+        g = w.pool_device(which, dev, chunk_elems=1 << 14).cpu().numpy().view(np.uint16)
+        assert np.array_equal(g, w.pool_bits(which))
+    torch.cuda.synchronize()
+
+
+def test_determinism_ten_runs():
+    dev = device()
+    w = W.make_workload("c3")
+    log("determinism: c3 x10, entry=pa_decode")
+    up = Uploaded(w, dev)
+    first = up.step().clone()
+    for _ in range(9):
+        again = up.step()
+        assert bool((again == first).all()), "decode output changed between identical runs"
+
+
+def test_batch_invariance_bitwise():
+    import torch
+    dev = device()
+    ctx = [700, 5, 1500, 33, 0, 260]
+    w = W.custom(seed=8, ctx_lens=ctx)
+    log(f"batch invariance ctx={ctx}")
+    up = Uploaded(w, dev)
+    full = up.step()[0].clone()
+    for b in range(len(ctx)):
+        out = B.decode(up.pool, up.q[0][b:b + 1].contiguous(), up.bt[0][b:b + 1].contiguous(),
+                       up.ctx[b:b + 1].contiguous(), float(w.scale))
+        assert bool((out[0] == full[b]).all()), f"sequence {b} differs alone vs in the batch"
+    # and inside a bigger, different batch
+    idx = torch.tensor([3, 2, 2, 0], device=dev)
+    out = B.decode(up.pool, up.q[0][idx].contiguous(), up.bt[0][idx].contiguous(),
+                   up.ctx[idx].contiguous(), float(w.scale))
+    assert bool((out == full[idx]).all())
+
+
+def test_page_permutation_invariance_bitwise():
+    import torch
+    dev = device()
+    w = W.custom(seed=9, ctx_lens=[900, 17, 1200], num_q_heads=28, num_kv_heads=4, head_dim=128)
+    log("page permutation invariance d=128")
+    up = Uploaded(w, dev)
+    base = up.step()[0].clone()
+    perm = torch.from_numpy(np.random.default_rng(1).permutation(w.num_pages)).to(dev)
+    k2 = torch.empty_like(up.k_pool)
+    v2 = torch.empty_like(up.v_pool)
+    k2[perm] = up.k_pool
+    v2[perm] = up.v_pool
+    pool2 = B.Pool(k2, v2)
+    bt2 = perm.to(torch.int32)[up.bt[0].long()].contiguous()
+    out = B.decode(pool2, up.q[0], bt2, up.ctx, float(w.scale))
+    assert bool((out == base).all()), "moving pages changed the output"
+
+
+def test_shared_pages_across_sequences():
+    """Two block tables naming the same pages (a shared prefix) read them read-only."""
+    import torch
+    dev = device()
+    w = W.custom(seed=10, ctx_lens=[640, 640], num_q_heads=32, num_kv_heads=8, head_dim=64)
+    log("shared pages")
+    up = Uploaded(w, dev)
+    bt = up.bt[0].clone()
+    bt[1, :20] = bt[0, :20]                  # first 320 tokens shared
+    q = up.q[0].clone()
+    out = B.decode(up.pool, q, bt, up.ctx, float(w.scale)).cpu().numpy()
+    ref = oracle.decode_attention(up.q_host[0], w.pool_bits("k"), w.pool_bits("v"),
+                                  bt.cpu().numpy(), w.ctx_lens, w.scale)
+    check_parity(out, ref, "shared pages")
+
+
+def test_one_token_returns_value_row_exactly():
+    dev = device()
+    for d, hq, hkv in [(64, 32, 8), (128, 28, 4)]:
+        w = W.custom(seed=11, ctx_lens=[1, 1, 1], num_q_heads=hq, num_kv_heads=hkv, head_dim=d)
+        log(f"ctx=1 exact d={d}")
+        up = Uploaded(w, dev)
+        out = up.step()[0].cpu().numpy()
+        v = w.pool_bits("v")
+        for b in range(3):
+            p = int(w.block_tables[0, b, 0])
+            for h in range(hq):
+                row = oracle.bf16_bits_to_f64(v[p, h // (hq // hkv), :, 0])
+                assert np.array_equal(out[b, h].astype(np.float64), row), (d, b, h)
+
+
+def test_append_bit_exact_and_nothing_else_changes():
+    import torch
+    dev = device()
+    for d, hq, hkv in [(64, 32, 8), (128, 28, 4)]:
+        ctx = [1, 16, 17, 40, 300, 33]
+        w = W.custom(seed=12, ctx_lens=ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                     append=True, extra_pages=5)
+        log(f"append d={d} positions={list(w.positions)} entry=pa_kv_append")
+        up = Uploaded(w, dev)
+        k0, v0 = w.pool_bits("k"), w.pool_bits("v")
+        pos = w.positions.copy()
+        pos[2] = -1                                     # skipped
+        pos_t = torch.from_numpy(pos).to(dev)
+        B.kv_append(up.pool, up.k_new[0], up.v_new[0], up.bt[0], pos_t)
+        k1 = up.k_pool.cpu().numpy().view(np.uint16)
+        v1 = up.v_pool.cpu().numpy().view(np.uint16)
+        ek, ev = oracle.kv_append(k0, v0, up.k_new_host[0], up.v_new_host[0], w.block_tables[0], pos)
+        assert np.array_equal(k1, ek), "K pool differs from the oracle's append"
+        assert np.array_equal(v1, ev), "V pool differs from the oracle's append"
+        # decode after append matches the oracle over ctx tokens (skipped seq: ctx - 1)
+        ctx_eff = w.ctx_lens.copy()
+        ctx_eff[2] -= 1
+        ctx_t = torch.from_numpy(ctx_eff).to(dev)
+        out = B.decode(up.pool, up.q[0], up.bt[0], ctx_t, float(w.scale)).cpu().numpy()
+        ref = oracle.decode_attention(up.q_host[0], ek, ev, w.block_tables[0], ctx_eff, w.scale)
+        check_parity(out, ref, f"decode after append d={d}")
+
+
+def test_out_of_range_inputs_stay_in_bounds():
+    """Page ids outside the pool and over-long contexts are clamped (no fault);
+    a position past the table or a bad page id makes the append skip."""
+    import torch
+    dev = device()
+    w = W.custom(seed=13, ctx_lens=[40, 20], num_q_heads=32, num_kv_heads=8, head_dim=64,
+                 append=True)
+    up = Uploaded(w, dev)
+    log("clamped inputs")
+    bt = up.bt[0].clone()
+    bt[0, 1] = w.num_pages + 1000
+    bt[1, 0] = -5
+    ctx = torch.tensor([10**6, 20], dtype=torch.int32, device=dev)
+    out = B.decode(up.pool, up.q[0], bt, ctx, float(w.scale))
+    torch.cuda.synchronize()
+    assert out.shape == (2, 32, 64)
+    k_before = up.k_pool.clone()
+    pos = torch.tensor([w.stride * 16, 0], dtype=torch.int32, device=dev)
+    B.kv_append(up.pool, up.k_new[0], up.v_new[0], bt, pos)     # seq 0: past the table; seq 1: page -5
+    torch.cuda.synchronize()
+    assert bool((up.k_pool == k_before).all())
+
+
+def test_error_paths_on_gpu():
+    import torch
+    dev = device()
+    w = W.custom(seed=14, ctx_lens=[600, 700])
+    up = Uploaded(w, dev)
+    log("error paths")
+    small = torch.empty(16, dtype=torch.uint8, device=dev)
+    with pytest.raises(B.PakvError) as e:
+        B.decode(up.pool, up.q[0], up.bt[0], up.ctx, 0.125, workspace=small)
+    assert e.value.status == 5
+    with pytest.raises(B.PakvError) as e:
+        B.decode(up.pool, up.q[0][:, :12].contiguous(), up.bt[0], up.ctx, 0.125)
+    assert e.value.status == 2
+
+
+def test_stream_read_helper():
+    import torch
+    dev = device()
+    buf = torch.ones(1 << 20, dtype=torch.int32, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    B.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink[0]) == 0
