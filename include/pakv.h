@@ -43,9 +43,9 @@
  *  - k_new, v_new: BF16 [num_seqs][num_kv_heads][head_dim]
  *  - block_tables: int32 [num_seqs][max_pages_per_seq] (one layer's table)
  *  - context_lens, positions: int32 [num_seqs]
- * Alignment: the pools, q, k_new, v_new and the workspace must be 16-byte
- * aligned (they are read with 16-byte loads); out and the int32 arrays need
- * 4-byte alignment.
+ * Alignment: the pools, q, out, k_new, v_new and the workspace must be
+ * 16-byte aligned (they are accessed with 16-byte loads and stores); the
+ * int32 arrays need 4-byte alignment.
  *
  * Device-resident data is not read by the host. Preconditions on it: page ids
  * in [0, num_pages); context_lens[b] in [0, max_pages_per_seq * 16]; the
@@ -140,6 +140,23 @@ pa_status pa_decode(const pa_pool* pool, const void* q, int32_t num_seqs,
                     int32_t max_pages_per_seq, const int32_t* context_lens,
                     float scale, float* out, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/*
+ * pa_kv_append followed by pa_decode, in one launch: decode adds the new
+ * token to the cache and then attends over it (samir-vllm README review;
+ * news-factory.app course article, KV-cache section). Arguments are those of
+ * the two calls; k_new / v_new / positions as in pa_kv_append. The pool after
+ * the call and `out` are bit-identical to those of the two separate calls.
+ * The workgroup whose split contains positions[b] writes the token before it
+ * reads any page, so context_lens[b] may include the new token (the usual
+ * case: positions[b] == context_lens[b] - 1).
+ */
+pa_status pa_decode_append(const pa_pool* pool, const void* q, const void* k_new,
+                           const void* v_new, const int32_t* positions, int32_t num_seqs,
+                           int32_t num_q_heads, const int32_t* block_tables,
+                           int32_t max_pages_per_seq, const int32_t* context_lens,
+                           float scale, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* Human-readable text for a status code (static storage). */
 const char* pa_status_str(pa_status status);

@@ -20,7 +20,7 @@ PA_OK = 0
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_INVALID", 3: "PA_ERR_UNSUPPORTED",
                 4: "PA_ERR_ALIGN", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_LAUNCH"}
 EXPORTS = ["pa_pool_create", "pa_pool_destroy", "pa_kv_append", "pa_decode_workspace_bytes",
-           "pa_split_tokens", "pa_decode", "pa_status_str", "pa_profile_start",
+           "pa_split_tokens", "pa_decode", "pa_decode_append", "pa_status_str", "pa_profile_start",
            "pa_profile_stop", "pa_stream_read"]
 
 _lib = None
@@ -56,6 +56,10 @@ def lib() -> ctypes.CDLL:
     L.pa_decode.argtypes = [c.c_void_p, c.c_void_p, c.c_int32, c.c_int32, c.c_void_p, c.c_int32,
                             c.c_void_p, c.c_float, c.c_void_p, c.c_void_p, c.c_size_t, c.c_void_p]
     L.pa_decode.restype = c.c_int
+    L.pa_decode_append.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
+                                   c.c_int32, c.c_int32, c.c_void_p, c.c_int32, c.c_void_p,
+                                   c.c_float, c.c_void_p, c.c_void_p, c.c_size_t, c.c_void_p]
+    L.pa_decode_append.restype = c.c_int
     L.pa_status_str.argtypes = [c.c_int]
     L.pa_status_str.restype = c.c_char_p
     L.pa_profile_start.argtypes = []
@@ -175,6 +179,32 @@ def decode(pool: Pool, q, block_tables, context_lens, scale: float, out=None, wo
     _check(lib().pa_decode(pool.handle, _ptr(q), num_seqs, num_q_heads, _ptr(block_tables), stride,
                            _ptr(context_lens), float(scale), _ptr(out), _ptr(workspace), ws_bytes,
                            _stream(stream)), "pa_decode")
+    return out
+
+
+def decode_append(pool: Pool, q, k_new, v_new, positions, block_tables, context_lens, scale: float,
+                  out=None, workspace=None, stream=None):
+    """Append each sequence's new token then decode, in one launch (pa_decode_append)."""
+    import torch
+    _need(q, "q", _bf16_types(), 3)
+    _need(k_new, "k_new", _bf16_types(), 3)
+    _need(v_new, "v_new", _bf16_types(), 3)
+    _need(positions, "positions", (torch.int32,), 1)
+    _need(block_tables, "block_tables", (torch.int32,), 2)
+    _need(context_lens, "context_lens", (torch.int32,), 1)
+    num_seqs, num_q_heads, d = q.shape
+    stride = block_tables.shape[1]
+    if out is None:
+        out = torch.empty((num_seqs, num_q_heads, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,), 3)
+    need = decode_workspace_bytes(pool, num_seqs, num_q_heads, stride)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode_append(pool.handle, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(positions),
+                                  num_seqs, num_q_heads, _ptr(block_tables), stride,
+                                  _ptr(context_lens), float(scale), _ptr(out), _ptr(workspace),
+                                  ws_bytes, _stream(stream)), "pa_decode_append")
     return out
 
 

@@ -16,13 +16,13 @@
 // Split geometry per head_dim: pages per split and wavefronts per workgroup.
 // Fixed per head_dim so that a sequence's result does not depend on the batch.
 #ifndef PAKV_SPLIT_PAGES_D64
-#define PAKV_SPLIT_PAGES_D64 32
+#define PAKV_SPLIT_PAGES_D64 64
 #endif
 #ifndef PAKV_WAVES_D64
 #define PAKV_WAVES_D64 4
 #endif
 #ifndef PAKV_SPLIT_PAGES_D128
-#define PAKV_SPLIT_PAGES_D128 32
+#define PAKV_SPLIT_PAGES_D128 64
 #endif
 #ifndef PAKV_WAVES_D128
 #define PAKV_WAVES_D128 4
@@ -106,14 +106,18 @@ struct LaunchTimer {
 
 template <int D, int W, int SP>
 pa_status launch_decode(const pakv::DecodeArgs& args, hipStream_t stream) {
+  (void)hipGetLastError();
   const int64_t blocks = static_cast<int64_t>(args.num_kv_heads) * args.num_seqs * args.s_max;
   if (blocks > INT_MAX) return PA_ERR_INVALID;
   const size_t lds = (2 * W * 16 + static_cast<size_t>(W) * args.group * (D + 4)) * sizeof(float);
-  (void)hipGetLastError();
   {
     LaunchTimer t(0, stream);
-    hipLaunchKernelGGL((pakv::decode_split_kernel<D, W, SP>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(64 * W), lds, stream, args);
+    if (args.k_new)
+      hipLaunchKernelGGL((pakv::decode_split_kernel<D, W, SP, true>), dim3(static_cast<unsigned>(blocks)),
+                         dim3(64 * W), lds, stream, args);
+    else
+      hipLaunchKernelGGL((pakv::decode_split_kernel<D, W, SP, false>), dim3(static_cast<unsigned>(blocks)),
+                         dim3(64 * W), lds, stream, args);
   }
   if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
   if (args.s_max > 1) {
@@ -204,7 +208,7 @@ pa_status pa_kv_append(const pa_pool* pool, const void* k_new, const void* v_new
   a.num_kv_heads = pool->num_kv_heads;
   a.stride = max_pages_per_seq;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const unsigned blocks = static_cast<unsigned>((num_seqs + 3) / 4);
+  const unsigned blocks = static_cast<unsigned>(num_seqs);
   (void)hipGetLastError();
   {
     LaunchTimer t(2, s);
@@ -217,10 +221,12 @@ pa_status pa_kv_append(const pa_pool* pool, const void* k_new, const void* v_new
   return PA_OK;
 }
 
-pa_status pa_decode(const pa_pool* pool, const void* q, int32_t num_seqs, int32_t num_q_heads,
-                    const int32_t* block_tables, int32_t max_pages_per_seq,
-                    const int32_t* context_lens, float scale, float* out, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+static pa_status decode_impl(const pa_pool* pool, const void* q, bool fused, const void* k_new,
+                             const void* v_new,
+                             const int32_t* positions, int32_t num_seqs, int32_t num_q_heads,
+                             const int32_t* block_tables, int32_t max_pages_per_seq,
+                             const int32_t* context_lens, float scale, float* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   if (!pool) return PA_ERR_NULL;
   if (num_seqs < 0 || num_q_heads < 1 || max_pages_per_seq < 1) return PA_ERR_INVALID;
   if (static_cast<int64_t>(max_pages_per_seq) * pakv::kPage > INT_MAX) return PA_ERR_INVALID;
@@ -230,8 +236,12 @@ pa_status pa_decode(const pa_pool* pool, const void* q, int32_t num_seqs, int32_
   if (group > kMaxGroup) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (!q || !block_tables || !context_lens || !out) return PA_ERR_NULL;
-  if (!aligned16(q) || !aligned4(block_tables) || !aligned4(context_lens) || !aligned4(out))
+  if (!aligned16(q) || !aligned4(block_tables) || !aligned4(context_lens) || !aligned16(out))
     return PA_ERR_ALIGN;
+  if (fused) {
+    if (!k_new || !v_new || !positions) return PA_ERR_NULL;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned4(positions)) return PA_ERR_ALIGN;
+  }
   const int d = pool->head_dim;
   size_t acc_bytes = 0, need = 0;
   workspace_parts(d, num_seqs, num_q_heads, max_pages_per_seq, &acc_bytes, &need);
@@ -256,9 +266,29 @@ pa_status pa_decode(const pa_pool* pool, const void* q, int32_t num_seqs, int32_
   a.stride = max_pages_per_seq;
   a.s_max = static_cast<int32_t>(splits_for(d, max_pages_per_seq));
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  a.k_new = fused ? static_cast<const uint16_t*>(k_new) : nullptr;
+  a.v_new = fused ? static_cast<const uint16_t*>(v_new) : nullptr;
+  a.positions = fused ? positions : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d == 64) return launch_decode<64, PAKV_WAVES_D64, PAKV_SPLIT_PAGES_D64>(a, s);
   return launch_decode<128, PAKV_WAVES_D128, PAKV_SPLIT_PAGES_D128>(a, s);
+}
+
+pa_status pa_decode(const pa_pool* pool, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                    const int32_t* block_tables, int32_t max_pages_per_seq,
+                    const int32_t* context_lens, float scale, float* out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return decode_impl(pool, q, false, nullptr, nullptr, nullptr, num_seqs, num_q_heads, block_tables,
+                     max_pages_per_seq, context_lens, scale, out, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_append(const pa_pool* pool, const void* q, const void* k_new, const void* v_new,
+                           const int32_t* positions, int32_t num_seqs, int32_t num_q_heads,
+                           const int32_t* block_tables, int32_t max_pages_per_seq,
+                           const int32_t* context_lens, float scale, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return decode_impl(pool, q, true, k_new, v_new, positions, num_seqs, num_q_heads, block_tables,
+                     max_pages_per_seq, context_lens, scale, out, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_profile_start(void) {

@@ -68,6 +68,11 @@ struct DecodeArgs {
   int32_t stride;     // max_pages_per_seq
   int32_t s_max;      // splits per sequence the grid covers
   float scale_log2;   // scale * log2(e)
+  // fused append (all NULL for a plain decode): the new token's K/V rows
+  // [B][Hkv][D] and their positions [B]
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int32_t* positions;
 };
 
 struct AppendArgs {
@@ -100,23 +105,307 @@ struct PairBuf {
 };
 
 // ---------------------------------------------------------------- decode
-template <int D, int W, int SPLIT_PAGES>
-__global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
-  static_assert(D == 64 || D == 128, "head_dim");
-  static_assert(SPLIT_PAGES % 2 == 0 && SPLIT_PAGES <= 64, "split pages: even, at most one per lane");
+// Per-lane constants for streaming one split of one (sequence, KV head).
+template <int D>
+struct SplitCtx {
+  const uint16_t* kbase;   // K pool + KV head tile + this lane's offset
+  const uint16_t* vbase;   // V pool + KV head tile + this lane's offset
+  size_t page_elems;       // elements per physical page in each pool
+  int my_pid;              // lane i: physical page of the split's logical page i
+  int npages;              // pages in this split
+  int pair_tok0;           // first token of the split
+  int tok1;                // one past the split's last token
+  bool k_second;           // this lane's K row lies in the pair's second page
+  bool v_second;           // this lane's V tokens lie in the pair's second page
+  float sl2;               // softmax scale * log2(e)
+  bf16x8 qf[D / 32];       // query group, MFMA B operand
+};
+
+// Running softmax state of one wave: head = lane % 16.
+template <int D>
+struct SoftmaxState {
+  float m;                 // running max (log2 units), same in the 4 lanes of a head
+  float l;                 // this lane's share of the running sum
+  f32x4 acc[D / 16];       // unnormalised output, dims 16 * mt + 4 * grp + i
+};
+
+template <int D>
+__device__ __forceinline__ void issue_pair(const SplitCtx<D>& c, PairBuf<D>& buf, int pr) {
   constexpr int KK = D / 32;
   constexpr int MT = D / 16;
-  constexpr int TILE = kPage * D;           // elements of one (page, kv head) tile
+  const int pa = __builtin_amdgcn_readlane(c.my_pid, 2 * pr);
+  const int pb = __builtin_amdgcn_readlane(c.my_pid, min(2 * pr + 1, c.npages - 1));  // a missing second page re-reads the first (all masked)
+  const uint16_t* kp = c.kbase + (size_t)(c.k_second ? pb : pa) * c.page_elems;
+  const uint16_t* vp = c.vbase + (size_t)(c.v_second ? pb : pa) * c.page_elems;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) buf.k[j][kk] = *(const u32x4*)(kp + 4 * j * D + 8 * kk);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) buf.v[mt] = *(const u32x4*)(vp + mt * 16 * kPage);
+  // keep later pairs' loads and this pair's math in program order, so the
+  // registers in use are the buffers as written
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int D>
+__device__ __forceinline__ void compute_pair(const SplitCtx<D>& c, PairBuf<D>& buf, int pr,
+                                             SoftmaxState<D>& st, int grp) {
+  constexpr int KK = D / 32;
+  constexpr int MT = D / 16;
+  const int pair_tok = c.pair_tok0 + 2 * kPage * pr;
+  f32x4 sc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    sc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf.k[j][kk]), c.qf[kk], sc[j], 0, 0, 0);
+  }
+  // scores in log2 units; tokens past the split end are masked by select
+  const int t_lane = pair_tok + 8 * grp;
+  float sv[8];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x = sc[j][i] * c.sl2;
+      x = (t_lane + 4 * j + i < c.tok1) ? x : -INFINITY;
+      sv[4 * j + i] = x;
+      mx = fmaxf(mx, x);
+    }
+  mx = xor_max(mx, 16);
+  mx = xor_max(mx, 32);
+  const float m_new = fmaxf(st.m, mx);
+  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+  float psum = 0.f;
+  bf16x8 ph, pl;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float p = __builtin_amdgcn_exp2f(sv[e] - m_new);
+    psum += p;
+    const __bf16 hi = (__bf16)p;
+    ph[e] = hi;
+    pl[e] = (__bf16)(p - (float)hi);
+  }
+  st.l = st.l * alpha + psum;
+  st.m = m_new;
+  if (__ballot(alpha != 1.f)) {   // skip the rescale when no head's max moved
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) st.acc[mt] *= alpha;
+  }
+  // tail pair: zero V of masked tokens (0 * NaN would poison the product)
+  if (pair_tok + 2 * kPage > c.tok1) {
+    int cnt = c.tok1 - t_lane;
+    cnt = cnt < 0 ? 0 : (cnt > 8 ? 8 : cnt);
+    uint32_t keep[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      keep[w] = (2 * w < cnt ? 0x0000FFFFu : 0u) | (2 * w + 1 < cnt ? 0xFFFF0000u : 0u);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) buf.v[mt][w] &= keep[w];
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    st.acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf.v[mt]), ph, st.acc[mt], 0, 0, 0);
+    st.acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf.v[mt]), pl, st.acc[mt], 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Stream pairs first, first + step, ... (< npairs) of a split into st. The
+// next pair's loads are in flight while the current one is computed (two
+// register buffers). The steady-state loop issues unconditionally and the last
+// one or two pairs are peeled, so every wait for loaded data counts exactly
+// the loads issued after it and never waits for the prefetch.
+template <int D>
+__device__ __forceinline__ void stream_pairs(const SplitCtx<D>& c, int first, int step, int npairs,
+                                             SoftmaxState<D>& st, int grp) {
+  const int my_n = first < npairs ? (npairs - first + step - 1) / step : 0;
+  if (my_n <= 0) return;
+  PairBuf<D> b0, b1;
+  issue_pair(c, b0, first);
+  int it = 0;
+  for (; it + 2 < my_n; it += 2) {
+    issue_pair(c, b1, first + (it + 1) * step);
+    compute_pair(c, b0, first + it * step, st, grp);
+    issue_pair(c, b0, first + (it + 2) * step);
+    compute_pair(c, b1, first + (it + 1) * step, st, grp);
+  }
+  if (it + 1 < my_n) {
+    issue_pair(c, b1, first + (it + 1) * step);
+    compute_pair(c, b0, first + it * step, st, grp);
+    compute_pair(c, b1, first + (it + 1) * step, st, grp);
+  } else {
+    compute_pair(c, b0, first + it * step, st, grp);
+  }
+}
+
+// Lane i's raw block-table entry for logical page s * SPLIT_PAGES + i (0 past
+// the row). Needs no context length, so it is loaded alongside it.
+template <int SPLIT_PAGES>
+__device__ __forceinline__ int load_split_pages(const DecodeArgs& a, int b, int s, int lane) {
+  const int p = s * SPLIT_PAGES + lane;
+  return (lane < SPLIT_PAGES && p < a.stride) ? a.block_tables[(size_t)b * a.stride + p] : 0;
+}
+
+template <int D, int SPLIT_PAGES>
+__device__ __forceinline__ void make_split_ctx(const DecodeArgs& a, int b, int kvh, int s, int n,
+                                               int lane, int raw_pid, SplitCtx<D>& c) {
+  constexpr int KK = D / 32;
+  constexpr int TILE = kPage * D;
+  constexpr int SPLIT_TOK = SPLIT_PAGES * kPage;
+  const int r = lane & 15;
+  const int grp = lane >> 4;
+  const int G = a.group;
+  const int tok0 = s * SPLIT_TOK;
+  c.tok1 = min(tok0 + SPLIT_TOK, n);
+  c.pair_tok0 = tok0;
+  const int p0 = tok0 / kPage;
+  c.npages = (c.tok1 - tok0 + kPage - 1) / kPage;
+  // this split's physical page ids, one per lane, clamped into the pool
+  (void)p0;
+  c.my_pid = lane < c.npages ? (raw_pid < 0 ? 0 : (raw_pid >= a.num_pages ? a.num_pages - 1 : raw_pid)) : 0;
+  // query group as the MFMA B operand (columns = heads, zero past G)
+  if (r < G) {
+    const uint16_t* qp = a.q + ((size_t)b * a.num_q_heads + (size_t)kvh * G + r) * D + (D / 4) * grp;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) c.qf[kk] = as_bf16x8(*(const u32x4*)(qp + 8 * kk));
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) c.qf[kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  }
+  c.page_elems = (size_t)a.num_kv_heads * TILE;
+  const int koff = (8 * ((r >> 2) & 1) + (r & 3)) * D + (D / 4) * grp;
+  const int voff = r * kPage + 8 * (grp & 1);
+  c.k_second = (r >> 3) != 0;
+  c.v_second = (grp >> 1) != 0;
+  c.kbase = a.kpool + (size_t)kvh * TILE + koff;
+  c.vbase = a.vpool + (size_t)kvh * TILE + voff;
+  c.sl2 = a.scale_log2;
+}
+
+template <int D>
+__device__ __forceinline__ void init_state(SoftmaxState<D>& st) {
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < D / 16; ++mt) st.acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Write one V column (the D values of one token) into a slot-minor V tile by
+// rewriting whole 32-byte slot rows: lane i handles rows i, i + 64, ...
+template <int D>
+__device__ __forceinline__ void write_v_column(uint16_t* vtile, const uint16_t* vn, int slot, int lane) {
+  const int w = (slot & 7) >> 1;
+  const int half = slot >> 3;
+  const uint32_t sh = (slot & 1) * 16;
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) {
+    const int dd = lane + 64 * i;
+    u32x4* row = (u32x4*)(vtile + (size_t)dd * kPage);
+    u32x4 h0 = row[0];
+    u32x4 h1 = row[1];
+    const uint32_t nv = vn[dd];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t upd0 = (h0[e] & ~(0xFFFFu << sh)) | (nv << sh);
+      const uint32_t upd1 = (h1[e] & ~(0xFFFFu << sh)) | (nv << sh);
+      h0[e] = (half == 0 && e == w) ? upd0 : h0[e];
+      h1[e] = (half == 1 && e == w) ? upd1 : h1[e];
+    }
+    row[0] = h0;
+    row[1] = h1;
+  }
+}
+
+// Fused append of a position the decode does not attend over (at or past the
+// context length): plain stores by wave 0 of the workgroup of the split the
+// position falls in; nothing in this launch reads that slot.
+template <int D>
+__device__ __forceinline__ void append_unattended(const DecodeArgs& a, int b, int kvh, int pos,
+                                                  int lane) {
+  const int pid = a.block_tables[(size_t)b * a.stride + pos / kPage];
+  if (pid < 0 || pid >= a.num_pages) return;
+  const int slot = pos % kPage;
+  const size_t tile = (size_t)pid * a.num_kv_heads + kvh;
+  const uint16_t* kn = a.k_new + ((size_t)b * a.num_kv_heads + kvh) * D;
+  const uint16_t* vn = a.v_new + ((size_t)b * a.num_kv_heads + kvh) * D;
+  uint16_t* kdst = const_cast<uint16_t*>(a.kpool) + (tile * kPage + slot) * D;
+  uint16_t* vdst = const_cast<uint16_t*>(a.vpool) + tile * D * kPage + slot;
+  if (lane < D / 8) *(u32x4*)(kdst + 8 * lane) = *(const u32x4*)(kn + 8 * lane);
+  write_v_column<D>(vdst - slot, vn, slot, lane);
+}
+
+// Fused append of an attended position, by the wave that will read its page
+// pair: every lane stores exactly the bytes of the new token that it loads
+// itself later (its chunks of the K row, its elements of the V column), so
+// program order within the lane makes its own later loads return them. No
+// other lane, wave or workgroup reads that slot in this launch, so no fence
+// or barrier is needed. pid is the token's page, p_in_pair 0/1 its page
+// within the pair, slot its slot.
+template <int D>
+__device__ __forceinline__ void append_by_reader(const DecodeArgs& a, int b, int kvh, int pid,
+                                                 int p_in_pair, int slot, int lane) {
+  constexpr int KK = D / 32;
+  constexpr int MT = D / 16;
+  const int r = lane & 15;
+  const int grp = lane >> 4;
+  const size_t tile = (size_t)pid * a.num_kv_heads + kvh;
+  const uint16_t* kn = a.k_new + ((size_t)b * a.num_kv_heads + kvh) * D;
+  const uint16_t* vn = a.v_new + ((size_t)b * a.num_kv_heads + kvh) * D;
+  // K: the QK row of this token is r = 8 * page-in-pair + 4 * (slot / 8) + slot % 4
+  if (r == 8 * p_in_pair + 4 * (slot >> 3) + (slot & 3)) {
+    uint16_t* kdst = const_cast<uint16_t*>(a.kpool) + (tile * kPage + slot) * D + (D / 4) * grp;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      *(u32x4*)(kdst + 8 * kk) = *(const u32x4*)(kn + (D / 4) * grp + 8 * kk);
+  }
+  // V: the two lane groups 2 * page-in-pair and 2 * page-in-pair + 1 load the
+  // two 16-byte halves of every 32-byte slot row of this page. They read their
+  // halves, put v_new into the token's element and write the halves back, so
+  // each row is written whole (a lone 2-byte write would make the memory side
+  // read-modify-write the sector).
+  if ((grp >> 1) == p_in_pair) {
+    const bool mine = (grp & 1) == (slot >> 3);
+    const int w = (slot & 7) >> 1;
+    const uint32_t sh = (slot & 1) * 16;
+    uint16_t* vrow = const_cast<uint16_t*>(a.vpool) + tile * D * kPage + r * kPage + 8 * (grp & 1);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      u32x4 h = *(const u32x4*)(vrow + mt * 16 * kPage);
+      const uint32_t nv = vn[16 * mt + r];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (mine && e == w) h[e] = (h[e] & ~(0xFFFFu << sh)) | (nv << sh);
+      *(u32x4*)(vrow + mt * 16 * kPage) = h;
+    }
+  }
+}
+
+// Waves per SIMD the register budget must allow (512 registers per lane).
+__host__ __device__ constexpr int occupancy(int d) { return d == 64 ? 4 : 2; }
+
+// Decode: one workgroup of W waves per (split, sequence, KV head); wave w
+// takes pairs w, w + W, ...; the waves merge through LDS. With FUSED the
+// launch also appends each sequence's new token (pa_decode_append).
+
+template <int D, int W, int SPLIT_PAGES, bool FUSED>
+__global__ __launch_bounds__(64 * W, occupancy(D)) void decode_split_kernel(DecodeArgs a) {
+  static_assert(D == 64 || D == 128, "head_dim");
+  static_assert(SPLIT_PAGES % 2 == 0 && SPLIT_PAGES <= 64, "split pages: even, at most one per lane");
+  constexpr int MT = D / 16;
   constexpr int SPLIT_TOK = SPLIT_PAGES * kPage;
   constexpr int LDS_ROW = D + 4;
-
   extern __shared__ float smem[];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15;
   const int grp = lane >> 4;
-
   const int wg = blockIdx.x;
   const int kvh = wg % a.num_kv_heads;
   const int rest = wg / a.num_kv_heads;
@@ -124,7 +413,22 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
   const int s = rest / a.num_seqs;
   const int G = a.group;
 
-  const int n = clamp_ctx(a.ctx[b], a.stride);
+  // the independent loads of the prologue are issued together
+  int pos = FUSED ? a.positions[b] : -1;
+  const int raw_pid = load_split_pages<SPLIT_PAGES>(a, b, s, lane);
+  const int ctx_b = a.ctx[b];
+  const int n = clamp_ctx(ctx_b, a.stride);
+  if (FUSED && pos >= 0 && pos < a.stride * kPage && pos / SPLIT_TOK == s) {
+    if (pos >= n) {
+      if (wave == 0) append_unattended<D>(a, b, kvh, pos, lane);
+    } else {
+      const int lp = pos / kPage - s * SPLIT_PAGES;          // page within this split
+      if (wave == (lp >> 1) % W) {                           // the wave reading its pair
+        const int v = __builtin_amdgcn_readlane(raw_pid, lp);
+        if (v >= 0 && v < a.num_pages) append_by_reader<D>(a, b, kvh, v, lp & 1, pos % kPage, lane);
+      }
+    }
+  }
   if (n == 0) {
     if (s == 0) {
       float* o = a.out + ((size_t)b * a.num_q_heads + (size_t)kvh * G) * D;
@@ -135,164 +439,31 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
   const int nsplit = (n + SPLIT_TOK - 1) / SPLIT_TOK;
   if (s >= nsplit) return;
 
-  const int tok0 = s * SPLIT_TOK;
-  const int tok1 = min(tok0 + SPLIT_TOK, n);
-  const int p0 = tok0 / kPage;
-  const int npages = (tok1 - tok0 + kPage - 1) / kPage;
-  const int npairs = (npages + 1) >> 1;
+  SplitCtx<D> c;
+  make_split_ctx<D, SPLIT_PAGES>(a, b, kvh, s, n, lane, raw_pid, c);
+  SoftmaxState<D> st;
+  init_state(st);
+  stream_pairs(c, wave, W, (c.npages + 1) >> 1, st, grp);
+  st.l += __shfl_xor(st.l, 16, 64);
+  st.l += __shfl_xor(st.l, 32, 64);
 
-  // This split's physical page ids, one per lane, clamped into the pool.
-  int my_pid = 0;
-  if (lane < npages) {
-    int v = a.block_tables[(size_t)b * a.stride + p0 + lane];
-    my_pid = v < 0 ? 0 : (v >= a.num_pages ? a.num_pages - 1 : v);
-  }
-
-  // Query group as the MFMA B operand (columns = heads, zero past G).
-  bf16x8 qf[KK];
-  if (r < G) {
-    const uint16_t* qp = a.q + ((size_t)b * a.num_q_heads + (size_t)kvh * G + r) * D + (D / 4) * grp;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qf[kk] = as_bf16x8(*(const u32x4*)(qp + 8 * kk));
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qf[kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-  }
-
-  const size_t page_elems = (size_t)a.num_kv_heads * TILE;
-  const int koff = (8 * ((r >> 2) & 1) + (r & 3)) * D + (D / 4) * grp;
-  const int voff = r * kPage + 8 * (grp & 1);
-  const bool k_second = (r >> 3) != 0;    // this lane's K row comes from the pair's second page
-  const bool v_second = (grp >> 1) != 0;  // this lane's V tokens come from the second page
-  const uint16_t* kbase = a.kpool + (size_t)kvh * TILE + koff;
-  const uint16_t* vbase = a.vpool + (size_t)kvh * TILE + voff;
-  const float sl2 = a.scale_log2;
-
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  f32x4 acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto issue = [&](PairBuf<D>& buf, int pr) {
-    const int la = 2 * pr;
-    const int lb = min(2 * pr + 1, npages - 1);     // a missing second page re-reads the first (all masked)
-    const int pa = __builtin_amdgcn_readlane(my_pid, la);
-    const int pb = __builtin_amdgcn_readlane(my_pid, lb);
-    const uint16_t* kp = kbase + (size_t)(k_second ? pb : pa) * page_elems;
-    const uint16_t* vp = vbase + (size_t)(v_second ? pb : pa) * page_elems;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) buf.k[j][kk] = *(const u32x4*)(kp + 4 * j * D + 8 * kk);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) buf.v[mt] = *(const u32x4*)(vp + mt * 16 * kPage);
-  };
-
-  auto compute = [&](PairBuf<D>& buf, int pr) {
-    const int pair_tok = (p0 + 2 * pr) * kPage;
-    f32x4 sc[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      sc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf.k[j][kk]), qf[kk], sc[j], 0, 0, 0);
-    }
-    // scores in log2 units; tokens past the split end are masked by select
-    const int t_lane = pair_tok + 8 * grp;
-    float sv[8];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = sc[j][i] * sl2;
-        x = (t_lane + 4 * j + i < tok1) ? x : -INFINITY;
-        sv[4 * j + i] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = xor_max(mx, 16);
-    mx = xor_max(mx, 32);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float psum = 0.f;
-    bf16x8 ph, pl;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = __builtin_amdgcn_exp2f(sv[e] - m_new);
-      psum += p;
-      const __bf16 hi = (__bf16)p;
-      ph[e] = hi;
-      pl[e] = (__bf16)(p - (float)hi);
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__ballot(alpha != 1.f)) {   // skip the rescale when no head's max moved
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
-    }
-    // tail pair: zero V of masked tokens (0 * NaN would poison the product)
-    if (pair_tok + 2 * kPage > tok1) {
-      int cnt = tok1 - t_lane;
-      cnt = cnt < 0 ? 0 : (cnt > 8 ? 8 : cnt);
-      uint32_t keep[4];
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        keep[w] = (2 * w < cnt ? 0x0000FFFFu : 0u) | (2 * w + 1 < cnt ? 0xFFFF0000u : 0u);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) buf.v[mt][w] &= keep[w];
-    }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf.v[mt]), ph, acc[mt], 0, 0, 0);
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf.v[mt]), pl, acc[mt], 0, 0, 0);
-    }
-  };
-
-  // This wave's pairs are wave, wave + W, ...; the next pair's loads are in
-  // flight while the current one is computed (two register buffers). The
-  // steady-state loop issues unconditionally and the last one or two pairs
-  // are peeled, so every wait for loaded data counts exactly the loads issued
-  // after it and never waits for the prefetch.
-  const int my_n = wave < npairs ? (npairs - wave + W - 1) / W : 0;
-  if (my_n > 0) {
-    PairBuf<D> b0, b1;
-    issue(b0, wave);
-    int it = 0;
-    for (; it + 2 < my_n; it += 2) {
-      issue(b1, wave + (it + 1) * W);
-      compute(b0, wave + it * W);
-      issue(b0, wave + (it + 2) * W);
-      compute(b1, wave + (it + 1) * W);
-    }
-    if (it + 1 < my_n) {
-      issue(b1, wave + (it + 1) * W);
-      compute(b0, wave + it * W);
-      compute(b1, wave + (it + 1) * W);
-    } else {
-      compute(b0, wave + it * W);
-    }
-  }
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-
-  // Merge the W waves through LDS: m, l per head, acc per (head, dim).
   float* sm_m = smem;
   float* sm_l = smem + W * 16;
   float* sm_acc = smem + 2 * W * 16;
   if (grp == 0) {
-    sm_m[wave * 16 + r] = m_run;
-    sm_l[wave * 16 + r] = l_run;
+    sm_m[wave * 16 + r] = st.m;
+    sm_l[wave * 16 + r] = st.l;
   }
   if (r < G) {
     float* dst = sm_acc + (size_t)(wave * G + r) * LDS_ROW + 4 * grp;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) *(f32x4*)(dst + 16 * mt) = acc[mt];
+    for (int mt = 0; mt < MT; ++mt) *(f32x4*)(dst + 16 * mt) = st.acc[mt];
   }
-  __syncthreads();
+  // LDS-only fences: the barrier must not wait for global stores in flight
+  // (a fused append's pool writes)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
   const bool alone = nsplit == 1;
   const size_t head0 = (size_t)b * a.num_q_heads + (size_t)kvh * G;
@@ -305,9 +476,9 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     float L = 0.f, A = 0.f;
 #pragma unroll
     for (int w = 0; w < W; ++w) {
-      const float c = __builtin_amdgcn_exp2f(sm_m[w * 16 + hh] - M);
-      L += c * sm_l[w * 16 + hh];
-      A += c * sm_acc[(size_t)(w * G + hh) * LDS_ROW + dd];
+      const float cw = __builtin_amdgcn_exp2f(sm_m[w * 16 + hh] - M);
+      L += cw * sm_l[w * 16 + hh];
+      A += cw * sm_acc[(size_t)(w * G + hh) * LDS_ROW + dd];
     }
     if (alone) {
       a.out[(head0 + hh) * D + dd] = A / L;
@@ -323,7 +494,19 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
 }
 
 // One wave per (sequence, query head): combine the splits of sequences that
-// have more than one, in split order.
+// have more than one, in split order. Lane i holds split i's (m, l) so all of
+// them arrive with one load; the partial outputs are read four splits at a time.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void merge_splits_kernel(DecodeArgs a, int split_tokens) {
   constexpr int PER = D / 64;
@@ -337,30 +520,55 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(DecodeArgs a, int spl
   const float* ml = a.ws_ml + (size_t)item * a.s_max * 2;
   const float* acc = a.ws_acc + (size_t)item * a.s_max * D;
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[2 * s]);
+  for (int s0 = 0; s0 < nsplit; s0 += 64)
+    if (s0 + lane < nsplit) M = fmaxf(M, ml[2 * (s0 + lane)]);
+  M = wave_max(M);
   float L = 0.f;
   float A[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) A[i] = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float c = __builtin_amdgcn_exp2f(ml[2 * s] - M);
-    L += c * ml[2 * s + 1];
+  for (int s0 = 0; s0 < nsplit; s0 += 64) {
+    const int cnt = min(64, nsplit - s0);
+    float c = 0.f;
+    if (lane < cnt) {
+      c = __builtin_amdgcn_exp2f(ml[2 * (s0 + lane)] - M);
+      L += c * ml[2 * (s0 + lane) + 1];
+    }
+    int j = 0;
+    for (; j + 4 <= cnt; j += 4) {
+      float v[4][PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) A[i] += c * acc[(size_t)s * D + lane + 64 * i];
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) v[u][i] = acc[(size_t)(s0 + j + u) * D + lane + 64 * i];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float cu = __shfl(c, j + u, 64);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) A[i] += cu * v[u][i];
+      }
+    }
+    for (; j < cnt; ++j) {
+      const float cu = __shfl(c, j, 64);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) A[i] += cu * acc[(size_t)(s0 + j) * D + lane + 64 * i];
+    }
   }
+  L = wave_sum(L);
+  const float inv = 1.f / L;
   float* o = a.out + (size_t)item * D;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) o[lane + 64 * i] = A[i] / L;
+  for (int i = 0; i < PER; ++i) o[lane + 64 * i] = A[i] * inv;
 }
 
 // ---------------------------------------------------------------- append
-// Four sequences per 256-thread block; a bit copy of the new token's K row
-// (16-byte stores) and V values (into the slot-minor V layout).
+// One 256-thread block per sequence: a bit copy of the new token's K row
+// (16-byte chunks) and of its V values into the slot-minor V layout, each V
+// slot row (32 bytes) read, patched and written whole.
 template <int D>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (b >= a.num_seqs) return;
+  const int t = threadIdx.x;
+  const int b = blockIdx.x;
   const int pos = a.positions[b];
   if (pos < 0 || pos >= a.stride * kPage) return;
   const int pid = a.block_tables[(size_t)b * a.stride + pos / kPage];
@@ -370,16 +578,29 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   const size_t tile0 = (size_t)pid * H;
   const uint16_t* kn = a.k_new + (size_t)b * H * D;
   const uint16_t* vn = a.v_new + (size_t)b * H * D;
-  for (int c = lane; c < H * (D / 8); c += 64) {
+  for (int c = t; c < H * (D / 8); c += 256) {
     const int g = c / (D / 8);
     const int part = c - g * (D / 8);
     *(u32x4*)(a.kpool + ((tile0 + g) * kPage + slot) * D + 8 * part) =
         *(const u32x4*)(kn + (size_t)g * D + 8 * part);
   }
-  for (int e = lane; e < H * D; e += 64) {
-    const int g = e / D;
-    const int dd = e - g * D;
-    a.vpool[((tile0 + g) * D + dd) * kPage + slot] = vn[e];
+  const int w = (slot & 7) >> 1;
+  const int half = slot >> 3;
+  const uint32_t sh = (slot & 1) * 16;
+  for (int e = t; e < H * D; e += 256) {     // row e = (kv head, dim)
+    u32x4* row = (u32x4*)(a.vpool + (tile0 * D + e) * kPage);
+    u32x4 h0 = row[0];
+    u32x4 h1 = row[1];
+    const uint32_t nv = vn[e];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t upd0 = (h0[i] & ~(0xFFFFu << sh)) | (nv << sh);
+      const uint32_t upd1 = (h1[i] & ~(0xFFFFu << sh)) | (nv << sh);
+      h0[i] = (half == 0 && i == w) ? upd0 : h0[i];
+      h1[i] = (half == 1 && i == w) ? upd1 : h1[i];
+    }
+    row[0] = h0;
+    row[1] = h1;
   }
 }
 

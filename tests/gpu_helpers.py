@@ -72,10 +72,16 @@ class Uploaded:
         self.out = torch.empty((w.num_layers, w.num_seqs, w.num_q_heads, w.head_dim),
                                dtype=torch.float32, device=dev)
 
-    def step(self, layers=None):
-        """One decode step: per layer, append (when the workload appends) then decode."""
+    def step(self, layers=None, fused=True):
+        """One decode step: per layer, append (when the workload appends) then
+        decode; fused=True uses the single-launch pa_decode_append."""
         w = self.w
         for layer in (range(w.num_layers) if layers is None else layers):
+            if w.append and fused:
+                B.decode_append(self.pool, self.q[layer], self.k_new[layer], self.v_new[layer],
+                                self.pos, self.bt[layer], self.ctx, float(w.scale),
+                                out=self.out[layer], workspace=self.workspace)
+                continue
             if w.append:
                 B.kv_append(self.pool, self.k_new[layer], self.v_new[layer], self.bt[layer], self.pos)
             B.decode(self.pool, self.q[layer], self.bt[layer], self.ctx, float(w.scale),

@@ -77,7 +77,7 @@ def test_decode_validation():
     assert f(scale=float("inf")) == INVALID
     assert f(scale=float("nan")) == INVALID
     assert f(q=MIS) == ALIGN
-    assert f(out=MIS + 2) == ALIGN
+    assert f(out=MIS) == ALIGN
     assert f(ctx=MIS + 1) == ALIGN
     assert f(ws=0) == WORKSPACE
     need = L.pa_decode_workspace_bytes(pool, 4, 32, 128)
@@ -85,6 +85,27 @@ def test_decode_validation():
     assert f(ws_bytes=need - 1) == WORKSPACE
     assert f(ws=MIS, ws_bytes=need) == ALIGN
     assert f(B=0) == OK                       # nothing to do, nothing queued
+    L.pa_pool_destroy(pool)
+
+
+def test_decode_append_validation():
+    L = B.lib()
+    pool = make_pool()
+    f = lambda **kw: L.pa_decode_append(kw.get("pool", pool), kw.get("q", P), kw.get("k", P),
+                                        kw.get("v", P), kw.get("pos", P), kw.get("B", 4),
+                                        kw.get("Hq", 32), kw.get("bt", P), kw.get("stride", 128),
+                                        kw.get("ctx", P), kw.get("scale", 0.125), kw.get("out", P),
+                                        kw.get("ws", P), kw.get("ws_bytes", 1 << 30), None)
+    assert f(pool=None) == NULL
+    assert f(k=0) == NULL
+    assert f(v=0) == NULL
+    assert f(pos=0) == NULL
+    assert f(q=0) == NULL
+    assert f(k=MIS) == ALIGN
+    assert f(pos=MIS + 2) == ALIGN
+    assert f(Hq=12) == INVALID
+    assert f(ws=0) == WORKSPACE
+    assert f(B=0) == OK
     L.pa_pool_destroy(pool)
 
 

@@ -132,6 +132,46 @@ def test_append_bit_exact_and_nothing_else_changes():
         check_parity(out, ref, f"decode after append d={d}")
 
 
+def test_fused_append_equals_separate_calls():
+    """pa_decode_append leaves the same pool bits and the same output bits as
+    pa_kv_append followed by pa_decode, for positions inside and past the
+    decoded context and for skipped sequences."""
+    import torch
+    dev = device()
+    for d, hq, hkv in [(64, 32, 8), (128, 28, 4)]:
+        ctx = [1, 16, 17, 1024, 1025, 2100, 40, 1000, 70]
+        w = W.custom(seed=15, ctx_lens=ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                     append=True, extra_pages=6)
+        log(f"fused vs separate d={d} ctx={ctx} entry=pa_decode_append")
+        pos = w.positions.copy()
+        pos[6] = -1                      # skipped
+        pos[2] = 3                       # rewrites a token inside the context
+        pos[7] = 5                       # early in a long context (not the last pair of its wave)
+        pos[8] = 90                      # past the decoded context (written, not attended)
+        pos_t = torch.from_numpy(pos).to(dev)
+        ctx_eff = w.ctx_lens.copy()
+        ctx_eff[6] -= 1                  # its last slot is never written
+        ctx_eff[2] = 16                  # its slot 16 is never written; token 3 is rewritten
+        ctx_eff[7] = 999                 # slot 999 never written
+        ctx_eff[8] = 69                  # slot 69 never written; 90 is written but not read
+        ctx_t = torch.from_numpy(ctx_eff).to(dev)
+        a = Uploaded(w, dev)
+        B.kv_append(a.pool, a.k_new[0], a.v_new[0], a.bt[0], pos_t)
+        out_a = B.decode(a.pool, a.q[0], a.bt[0], ctx_t, float(w.scale))
+        b = Uploaded(w, dev)
+        out_b = B.decode_append(b.pool, b.q[0], b.k_new[0], b.v_new[0], pos_t, b.bt[0], ctx_t,
+                                float(w.scale))
+        assert bool((a.k_pool == b.k_pool).all()) and bool((a.v_pool == b.v_pool).all())
+        assert bool((out_a.view(torch.int32) == out_b.view(torch.int32)).all()), \
+            "fused output differs from the two-call output"
+        ek, ev = oracle.kv_append(w.pool_bits("k"), w.pool_bits("v"), b.k_new_host[0], b.v_new_host[0],
+                                  w.block_tables[0], pos)
+        assert np.array_equal(b.k_pool.cpu().numpy().view(np.uint16), ek)
+        assert np.array_equal(b.v_pool.cpu().numpy().view(np.uint16), ev)
+        ref = oracle.decode_attention(b.q_host[0], ek, ev, w.block_tables[0], ctx_eff, w.scale)
+        check_parity(out_b.cpu().numpy(), ref, f"fused d={d}")
+
+
 def test_out_of_range_inputs_stay_in_bounds():
     """Page ids outside the pool and over-long contexts are clamped (no fault);
     a position past the table or a bad page id makes the append skip."""
@@ -158,7 +198,7 @@ def test_out_of_range_inputs_stay_in_bounds():
 def test_error_paths_on_gpu():
     import torch
     dev = device()
-    w = W.custom(seed=14, ctx_lens=[600, 700])
+    w = W.custom(seed=14, ctx_lens=[2500, 700])         # more than one split: needs workspace
     up = Uploaded(w, dev)
     log("error paths")
     small = torch.empty(16, dtype=torch.uint8, device=dev)
