@@ -28,6 +28,27 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E peak
 MALL_BYTES = 256 << 20   # device last-level (Infinity) cache
+PROFILE = os.path.join(ROOT, "profiles", "decode_split_kernel_c4.md")
+KERNEL_SOURCES = ("paged_kv_decode_02_amd/csrc/pakv_kernels.h", "paged_kv_decode_02_amd/csrc/pakv.hip")
+
+
+def counted_traffic(workload):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    only if it was taken on this workload with the kernel sources as they are
+    now (sha256 of the sources); None otherwise."""
+    import hashlib
+    if workload != "c4" or not os.path.exists(PROFILE):
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    for line in open(PROFILE):
+        if line.startswith("traffic_json:"):
+            t = json.loads(line.split(":", 1)[1])
+            if t.get("source_sha256") == h.hexdigest():
+                return t
+    return None
 
 
 def parse():
@@ -218,6 +239,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
 
+    traffic = counted_traffic(w.name)
     result = {
         "metric": "paged decode attention: achieved KV-read GB/s (% of HBM peak) + us/step",
         "value": round(value, 1),
@@ -259,7 +281,10 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": traffic["traffic_bytes_per_launch"] if traffic else None,
+            "traffic_detail": ({"fetch_bytes": traffic["fetch_bytes_per_launch"],
+                                "write_bytes": traffic["write_bytes_per_launch"],
+                                "source": "profiles/decode_split_kernel_c4.md"} if traffic else None),
             "avg_launch_us": round(dec_avg_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": w.kv_bytes_per_layer(),
         },
