@@ -79,6 +79,16 @@ class Inputs:
             self.k_new = torch.from_numpy(w.new_kv_bits("k").view(np.int16)).to(dev)
             self.v_new = torch.from_numpy(w.new_kv_bits("v").view(np.int16)).to(dev)
             self.pos = torch.from_numpy(w.positions).to(dev)
+        # launch plan: made on the host from the host copy of the context
+        # lengths once per step (every layer shares it), copied to the device
+        # from pinned memory; two host buffers so that the plan of the next
+        # step is never written while the previous copy may still read it
+        self.ctx_host = w.ctx_lens.copy()
+        cap = B.decode_plan_capacity(self.pool, w.num_seqs, w.stride)
+        self.plan_pin = [torch.empty(cap, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self.plan_copied = [None, None]
+        self.plan_dev = torch.empty(cap, dtype=torch.int32, device=dev)
+        self.step_no = 0
         need = B.decode_workspace_bytes(self.pool, w.num_seqs, w.num_q_heads, w.stride)
         self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
         self.out = torch.empty((w.num_layers, w.num_seqs, w.num_q_heads, w.head_dim),
@@ -86,15 +96,29 @@ class Inputs:
 
 
 def run_step(w, x, B, stream):
-    """One step: per layer, the paged append of the new token's K/V
-    (pa_kv_append) then paged decode attention (pa_decode). The single-launch
+    """One step: the launch plan for this step's context lengths (host, then an
+    async copy to the device), then per layer the paged append of the new
+    token's K/V (pa_kv_append) and paged decode attention driven by the plan
+    (pa_decode_planned, bit-identical to pa_decode). The single-launch
     pa_decode_append gives bit-identical results but measures slower, so the
     step uses the two calls."""
+    import torch
+    k = x.step_no & 1
+    x.step_no += 1
+    if x.plan_copied[k] is not None:
+        x.plan_copied[k].synchronize()
+    n = B.decode_plan_into(x.pool, x.ctx_host, w.stride, x.plan_pin[k])
+    plan = x.plan_dev[:n]
+    with torch.cuda.stream(stream):
+        plan.copy_(x.plan_pin[k][:n], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        x.plan_copied[k] = ev
     for layer in range(w.num_layers):
         if w.append:
             B.kv_append(x.pool, x.k_new[layer], x.v_new[layer], x.bt[layer], x.pos, stream=stream)
-        B.decode(x.pool, x.q[layer], x.bt[layer], x.ctx, float(w.scale), out=x.out[layer],
-                 workspace=x.ws, stream=stream)
+        B.decode_planned(x.pool, x.q[layer], x.bt[layer], x.ctx, float(w.scale), plan,
+                         out=x.out[layer], workspace=x.ws, stream=stream)
 
 
 def stream_ceiling(B, dev, stream):

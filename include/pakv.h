@@ -158,6 +158,47 @@ pa_status pa_decode_append(const pa_pool* pool, const void* q, const void* k_new
                            float scale, float* out, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/*
+ * Launch plan (host side, optional). The workgroups of pa_decode cover every
+ * (sequence, split) the batch could have, in split-major order; most of them
+ * find their split empty when contexts are short next to max_pages_per_seq,
+ * and the largest splits of the longest sequences start last. A plan lists
+ * only the splits that exist, largest first (page count descending; ties in
+ * sequence order, then split order; a sequence with an empty context keeps
+ * one item, last, which writes its zero output). Serving code knows its
+ * context lengths on the host, and one plan serves every layer of a step.
+ *
+ * pa_decode_plan_capacity: items a plan may need for these sizes
+ * (num_seqs * splits per sequence), or -1 when the sizes are out of range
+ * (num_seqs above 2^20, or more than 2^11 splits per sequence).
+ * pa_decode_plan: writes the plan for the host array context_lens_host
+ * [num_seqs] (values clamped into [0, max_pages_per_seq * 16], as the
+ * kernel does) into plan[capacity] (host memory) and its length into
+ * *num_items. Item encoding: b | (split << 20). Pure host code; queues
+ * nothing.
+ */
+int64_t pa_decode_plan_capacity(const pa_pool* pool, int32_t num_seqs,
+                                int32_t max_pages_per_seq);
+pa_status pa_decode_plan(const pa_pool* pool, const int32_t* context_lens_host,
+                         int32_t num_seqs, int32_t max_pages_per_seq, int32_t* plan,
+                         int64_t capacity, int32_t* num_items);
+
+/*
+ * pa_decode driven by a plan: the same arguments, plus plan (device memory,
+ * int32 [num_items], a copy of what pa_decode_plan wrote) and num_items.
+ * The output is bit-identical to pa_decode's when the plan was made from the
+ * same context lengths (the splits, and the order in which they are merged,
+ * do not change). A plan made from other lengths leaves the output of the
+ * sequences it misses unwritten; items naming a sequence or split out of
+ * range are skipped on the device.
+ */
+pa_status pa_decode_planned(const pa_pool* pool, const void* q, int32_t num_seqs,
+                            int32_t num_q_heads, const int32_t* block_tables,
+                            int32_t max_pages_per_seq, const int32_t* context_lens,
+                            float scale, float* out, void* workspace,
+                            size_t workspace_bytes, const int32_t* plan,
+                            int32_t num_items, void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* pa_status_str(pa_status status);
 

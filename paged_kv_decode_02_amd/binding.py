@@ -17,11 +17,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpakv.so")
 
 PA_OK = 0
+PA_ERR_INVALID = 2
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_INVALID", 3: "PA_ERR_UNSUPPORTED",
                 4: "PA_ERR_ALIGN", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_LAUNCH"}
 EXPORTS = ["pa_pool_create", "pa_pool_destroy", "pa_kv_append", "pa_decode_workspace_bytes",
            "pa_split_tokens", "pa_decode", "pa_decode_append", "pa_status_str", "pa_profile_start",
-           "pa_profile_stop", "pa_stream_read"]
+           "pa_profile_stop", "pa_stream_read", "pa_decode_plan_capacity", "pa_decode_plan",
+           "pa_decode_planned"]
 
 _lib = None
 
@@ -68,6 +70,15 @@ def lib() -> ctypes.CDLL:
     L.pa_profile_stop.restype = c.c_int
     L.pa_stream_read.argtypes = [c.c_void_p, c.c_size_t, c.c_void_p, c.c_void_p]
     L.pa_stream_read.restype = c.c_int
+    L.pa_decode_plan_capacity.argtypes = [c.c_void_p, c.c_int32, c.c_int32]
+    L.pa_decode_plan_capacity.restype = c.c_int64
+    L.pa_decode_plan.argtypes = [c.c_void_p, c.c_void_p, c.c_int32, c.c_int32, c.c_void_p, c.c_int64,
+                                 c.POINTER(c.c_int32)]
+    L.pa_decode_plan.restype = c.c_int
+    L.pa_decode_planned.argtypes = [c.c_void_p, c.c_void_p, c.c_int32, c.c_int32, c.c_void_p, c.c_int32,
+                                    c.c_void_p, c.c_float, c.c_void_p, c.c_void_p, c.c_size_t,
+                                    c.c_void_p, c.c_int32, c.c_void_p]
+    L.pa_decode_planned.restype = c.c_int
     _lib = L
     return L
 
@@ -179,6 +190,71 @@ def decode(pool: Pool, q, block_tables, context_lens, scale: float, out=None, wo
     _check(lib().pa_decode(pool.handle, _ptr(q), num_seqs, num_q_heads, _ptr(block_tables), stride,
                            _ptr(context_lens), float(scale), _ptr(out), _ptr(workspace), ws_bytes,
                            _stream(stream)), "pa_decode")
+    return out
+
+
+def decode_plan_capacity(pool: Pool, num_seqs: int, max_pages_per_seq: int) -> int:
+    cap = int(lib().pa_decode_plan_capacity(pool.handle, int(num_seqs), int(max_pages_per_seq)))
+    if cap < 0:
+        raise PakvError(PA_ERR_INVALID, "pa_decode_plan_capacity")
+    return cap
+
+
+def decode_plan_into(pool: Pool, context_lens_host, max_pages_per_seq: int, out) -> int:
+    """Write the launch plan for these host context lengths into ``out`` (host
+    int32 memory: a numpy array or a CPU torch tensor, e.g. pinned, of at least
+    decode_plan_capacity items); returns the number of items (pa_decode_plan)."""
+    import numpy as np
+    ctx = np.ascontiguousarray(np.asarray(context_lens_host, dtype=np.int32))
+    if ctx.ndim != 1:
+        raise ValueError("context_lens_host must be 1-D")
+    if isinstance(out, np.ndarray):
+        if out.dtype != np.int32 or not out.flags.c_contiguous:
+            raise ValueError("out must be a contiguous int32 array")
+        addr, size = out.ctypes.data, out.size
+    else:
+        import torch
+        if out.dtype != torch.int32 or out.is_cuda or not out.is_contiguous():
+            raise ValueError("out must be a contiguous host int32 tensor")
+        addr, size = out.data_ptr(), out.numel()
+    n = ctypes.c_int32(0)
+    _check(lib().pa_decode_plan(pool.handle, ctx.ctypes.data, ctx.size, int(max_pages_per_seq),
+                                addr, size, ctypes.byref(n)), "pa_decode_plan")
+    return n.value
+
+
+def decode_plan(pool: Pool, context_lens_host, max_pages_per_seq: int):
+    """Host-side launch plan for these context lengths (pa_decode_plan): an int32
+    numpy array of items ``b | split << 20``, largest split first."""
+    import numpy as np
+    num_seqs = np.asarray(context_lens_host).size
+    plan = np.zeros(max(decode_plan_capacity(pool, num_seqs, max_pages_per_seq), 1), dtype=np.int32)
+    n = decode_plan_into(pool, context_lens_host, max_pages_per_seq, plan)
+    return plan[:n].copy()
+
+
+def decode_planned(pool: Pool, q, block_tables, context_lens, scale: float, plan, out=None,
+                   workspace=None, stream=None):
+    """pa_decode driven by a launch plan (pa_decode_planned); ``plan`` is a device
+    int32 tensor holding what decode_plan returned for the same lengths."""
+    import torch
+    _need(q, "q", _bf16_types(), 3)
+    _need(block_tables, "block_tables", (torch.int32,), 2)
+    _need(context_lens, "context_lens", (torch.int32,), 1)
+    _need(plan, "plan", (torch.int32,), 1)
+    num_seqs, num_q_heads, d = q.shape
+    stride = block_tables.shape[1]
+    if out is None:
+        out = torch.empty((num_seqs, num_q_heads, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,), 3)
+    need = decode_workspace_bytes(pool, num_seqs, num_q_heads, stride)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode_planned(pool.handle, _ptr(q), num_seqs, num_q_heads, _ptr(block_tables),
+                                   stride, _ptr(context_lens), float(scale), _ptr(out), _ptr(workspace),
+                                   ws_bytes, _ptr(plan), plan.numel(), _stream(stream)),
+           "pa_decode_planned")
     return out
 
 

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -39,6 +40,8 @@ struct pa_pool {
 namespace {
 
 constexpr int kMaxGroup = 16;   // query heads per KV head: the 16 MFMA columns
+constexpr int64_t kPlanMaxSeqs = 1 << 20;   // plan items pack b in 20 bits
+constexpr int64_t kPlanMaxSplits = 1 << 11; // and the split in the 11 above them
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -105,9 +108,10 @@ struct LaunchTimer {
 };
 
 template <int D, int W, int SP>
-pa_status launch_decode(const pakv::DecodeArgs& args, hipStream_t stream) {
+pa_status launch_decode(const pakv::DecodeArgs& args, int64_t units, hipStream_t stream) {
   (void)hipGetLastError();
-  const int64_t blocks = static_cast<int64_t>(args.num_kv_heads) * args.num_seqs * args.s_max;
+  const int64_t blocks = static_cast<int64_t>(args.num_kv_heads) * units;
+  if (blocks == 0) return PA_OK;
   if (blocks > INT_MAX) return PA_ERR_INVALID;
   const size_t lds = (2 * W * 16 + static_cast<size_t>(W) * args.group * (D + 4)) * sizeof(float);
   {
@@ -226,7 +230,8 @@ static pa_status decode_impl(const pa_pool* pool, const void* q, bool fused, con
                              const int32_t* positions, int32_t num_seqs, int32_t num_q_heads,
                              const int32_t* block_tables, int32_t max_pages_per_seq,
                              const int32_t* context_lens, float scale, float* out, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+                             size_t workspace_bytes, const int32_t* plan, int32_t plan_items,
+                             void* stream) {
   if (!pool) return PA_ERR_NULL;
   if (num_seqs < 0 || num_q_heads < 1 || max_pages_per_seq < 1) return PA_ERR_INVALID;
   if (static_cast<int64_t>(max_pages_per_seq) * pakv::kPage > INT_MAX) return PA_ERR_INVALID;
@@ -243,6 +248,13 @@ static pa_status decode_impl(const pa_pool* pool, const void* q, bool fused, con
     if (!aligned16(k_new) || !aligned16(v_new) || !aligned4(positions)) return PA_ERR_ALIGN;
   }
   const int d = pool->head_dim;
+  const int64_t s_max = splits_for(d, max_pages_per_seq);
+  if (num_seqs > kPlanMaxSeqs || s_max > kPlanMaxSplits) {
+    if (plan) return PA_ERR_INVALID;
+  }
+  if (plan_items < 0 || plan_items > static_cast<int64_t>(num_seqs) * s_max) return PA_ERR_INVALID;
+  if (plan_items > 0 && !plan) return PA_ERR_NULL;
+  if (plan && !aligned4(plan)) return PA_ERR_ALIGN;
   size_t acc_bytes = 0, need = 0;
   workspace_parts(d, num_seqs, num_q_heads, max_pages_per_seq, &acc_bytes, &need);
   if (need > 0) {
@@ -269,9 +281,11 @@ static pa_status decode_impl(const pa_pool* pool, const void* q, bool fused, con
   a.k_new = fused ? static_cast<const uint16_t*>(k_new) : nullptr;
   a.v_new = fused ? static_cast<const uint16_t*>(v_new) : nullptr;
   a.positions = fused ? positions : nullptr;
+  a.plan = plan;
+  const int64_t units = plan ? plan_items : static_cast<int64_t>(num_seqs) * s_max;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (d == 64) return launch_decode<64, PAKV_WAVES_D64, PAKV_SPLIT_PAGES_D64>(a, s);
-  return launch_decode<128, PAKV_WAVES_D128, PAKV_SPLIT_PAGES_D128>(a, s);
+  if (d == 64) return launch_decode<64, PAKV_WAVES_D64, PAKV_SPLIT_PAGES_D64>(a, units, s);
+  return launch_decode<128, PAKV_WAVES_D128, PAKV_SPLIT_PAGES_D128>(a, units, s);
 }
 
 pa_status pa_decode(const pa_pool* pool, const void* q, int32_t num_seqs, int32_t num_q_heads,
@@ -279,7 +293,76 @@ pa_status pa_decode(const pa_pool* pool, const void* q, int32_t num_seqs, int32_
                     const int32_t* context_lens, float scale, float* out, void* workspace,
                     size_t workspace_bytes, void* stream) {
   return decode_impl(pool, q, false, nullptr, nullptr, nullptr, num_seqs, num_q_heads, block_tables,
-                     max_pages_per_seq, context_lens, scale, out, workspace, workspace_bytes, stream);
+                     max_pages_per_seq, context_lens, scale, out, workspace, workspace_bytes, nullptr,
+                     0, stream);
+}
+
+int64_t pa_decode_plan_capacity(const pa_pool* pool, int32_t num_seqs, int32_t max_pages_per_seq) {
+  if (!pool || num_seqs < 0 || max_pages_per_seq < 1) return -1;
+  const int64_t s_max = splits_for(pool->head_dim, max_pages_per_seq);
+  if (num_seqs > kPlanMaxSeqs || s_max > kPlanMaxSplits) return -1;
+  return static_cast<int64_t>(num_seqs) * s_max;
+}
+
+pa_status pa_decode_plan(const pa_pool* pool, const int32_t* context_lens_host, int32_t num_seqs,
+                         int32_t max_pages_per_seq, int32_t* plan, int64_t capacity,
+                         int32_t* num_items) {
+  if (!pool || !num_items) return PA_ERR_NULL;
+  *num_items = 0;
+  const int64_t cap_needed = pa_decode_plan_capacity(pool, num_seqs, max_pages_per_seq);
+  if (cap_needed < 0) return PA_ERR_INVALID;
+  if (num_seqs == 0) return PA_OK;
+  if (!context_lens_host || !plan) return PA_ERR_NULL;
+  const int sp = split_pages(pool->head_dim);
+  const int64_t max_tok = static_cast<int64_t>(max_pages_per_seq) * pakv::kPage;
+  // pages of every split, then a counting sort by page count, largest first
+  // (ties in sequence order, then split order); an empty context keeps one
+  // unit (it writes the zero output) and goes last
+  std::vector<int64_t> count(sp + 2, 0);
+  int64_t total = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t n = std::min<int64_t>(std::max(context_lens_host[b], 0), max_tok);
+    const int64_t pages = (n + pakv::kPage - 1) / pakv::kPage;
+    if (pages == 0) {
+      ++count[0];
+      ++total;
+      continue;
+    }
+    const int64_t ns = (pages + sp - 1) / sp;
+    count[sp] += ns - 1;
+    ++count[pages - (ns - 1) * sp];
+    total += ns;
+  }
+  if (total > capacity) return PA_ERR_INVALID;
+  std::vector<int64_t> start(sp + 2, 0);
+  int64_t acc = 0;
+  for (int pg = sp; pg >= 0; --pg) {
+    start[pg] = acc;
+    acc += count[pg];
+  }
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t n = std::min<int64_t>(std::max(context_lens_host[b], 0), max_tok);
+    const int64_t pages = (n + pakv::kPage - 1) / pakv::kPage;
+    const int64_t ns = pages == 0 ? 1 : (pages + sp - 1) / sp;
+    for (int64_t s = 0; s < ns; ++s) {
+      const int64_t pg = std::min<int64_t>(pages - s * sp, sp);
+      plan[start[pg]++] = static_cast<int32_t>(static_cast<uint32_t>(b) | (static_cast<uint32_t>(s) << 20));
+    }
+  }
+  *num_items = static_cast<int32_t>(total);
+  return PA_OK;
+}
+
+pa_status pa_decode_planned(const pa_pool* pool, const void* q, int32_t num_seqs,
+                            int32_t num_q_heads, const int32_t* block_tables,
+                            int32_t max_pages_per_seq, const int32_t* context_lens, float scale,
+                            float* out, void* workspace, size_t workspace_bytes,
+                            const int32_t* plan, int32_t num_items, void* stream) {
+  if (!pool) return PA_ERR_NULL;
+  if (!plan && num_seqs > 0) return PA_ERR_NULL;
+  return decode_impl(pool, q, false, nullptr, nullptr, nullptr, num_seqs, num_q_heads, block_tables,
+                     max_pages_per_seq, context_lens, scale, out, workspace, workspace_bytes, plan,
+                     num_items, stream);
 }
 
 pa_status pa_decode_append(const pa_pool* pool, const void* q, const void* k_new, const void* v_new,
@@ -288,7 +371,8 @@ pa_status pa_decode_append(const pa_pool* pool, const void* q, const void* k_new
                            const int32_t* context_lens, float scale, float* out, void* workspace,
                            size_t workspace_bytes, void* stream) {
   return decode_impl(pool, q, true, k_new, v_new, positions, num_seqs, num_q_heads, block_tables,
-                     max_pages_per_seq, context_lens, scale, out, workspace, workspace_bytes, stream);
+                     max_pages_per_seq, context_lens, scale, out, workspace, workspace_bytes, nullptr,
+                     0, stream);
 }
 
 pa_status pa_profile_start(void) {

@@ -73,6 +73,9 @@ struct DecodeArgs {
   const uint16_t* k_new;
   const uint16_t* v_new;
   const int32_t* positions;
+  // optional launch plan: workgroup (item, KV head) takes the split
+  // plan[item] = b | s << 20; NULL = every (sequence, split) in split-major order
+  const int32_t* plan;
 };
 
 struct AppendArgs {
@@ -409,8 +412,16 @@ __global__ __launch_bounds__(64 * W, occupancy(D)) void decode_split_kernel(Deco
   const int wg = blockIdx.x;
   const int kvh = wg % a.num_kv_heads;
   const int rest = wg / a.num_kv_heads;
-  const int b = rest % a.num_seqs;
-  const int s = rest / a.num_seqs;
+  int b, s;
+  if (a.plan) {
+    const uint32_t item = (uint32_t)a.plan[rest];
+    b = (int)(item & 0xFFFFFu);
+    s = (int)(item >> 20);
+    if (b >= a.num_seqs || s >= a.s_max) return;
+  } else {
+    b = rest % a.num_seqs;
+    s = rest / a.num_seqs;
+  }
   const int G = a.group;
 
   // the independent loads of the prologue are issued together

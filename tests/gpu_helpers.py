@@ -72,10 +72,15 @@ class Uploaded:
         self.out = torch.empty((w.num_layers, w.num_seqs, w.num_q_heads, w.head_dim),
                                dtype=torch.float32, device=dev)
 
-    def step(self, layers=None, fused=True):
+    def step(self, layers=None, fused=True, planned=False):
         """One decode step: per layer, append (when the workload appends) then
-        decode; fused=True uses the single-launch pa_decode_append."""
+        decode; fused=True uses the single-launch pa_decode_append, planned=True
+        (with fused=False) pa_decode_planned with the host-made launch plan."""
+        import torch
         w = self.w
+        plan = None
+        if planned:
+            plan = torch.from_numpy(B.decode_plan(self.pool, w.ctx_lens, w.stride)).to(self.dev)
         for layer in (range(w.num_layers) if layers is None else layers):
             if w.append and fused:
                 B.decode_append(self.pool, self.q[layer], self.k_new[layer], self.v_new[layer],
@@ -84,6 +89,10 @@ class Uploaded:
                 continue
             if w.append:
                 B.kv_append(self.pool, self.k_new[layer], self.v_new[layer], self.bt[layer], self.pos)
+            if plan is not None:
+                B.decode_planned(self.pool, self.q[layer], self.bt[layer], self.ctx, float(w.scale), plan,
+                                 out=self.out[layer], workspace=self.workspace)
+                continue
             B.decode(self.pool, self.q[layer], self.bt[layer], self.ctx, float(w.scale),
                      out=self.out[layer], workspace=self.workspace)
         return self.out

@@ -155,3 +155,79 @@ def test_profile_and_status_strings():
         assert B.status_str(s)
     assert L.pa_stream_read(P, 15, P2, None) == INVALID
     assert L.pa_stream_read(0, 16, P2, None) == NULL
+
+
+# ---- launch plan (pure host code)
+
+def expected_plan(ctx, stride, split_pages=64):
+    """Every (sequence, split) that exists, sorted by page count descending, then
+    sequence, then split; an empty context keeps one zero-page item."""
+    items = []
+    for b, n in enumerate(ctx):
+        n = min(max(int(n), 0), stride * 16)
+        pages = (n + 15) // 16
+        if pages == 0:
+            items.append((0, b, 0))
+            continue
+        for s in range((pages + split_pages - 1) // split_pages):
+            items.append((min(pages - s * split_pages, split_pages), b, s))
+    items.sort(key=lambda t: (-t[0], t[1], t[2]))
+    return [b | (s << 20) for _, b, s in items]
+
+
+def test_plan_order_and_clamping():
+    import numpy as np
+    L = B.lib()
+    h = make_pool(d=64)
+    pool = type("P", (), {"handle": h})()
+    rng = np.random.default_rng(7)
+    for stride in (1, 5, 64, 65, 512):
+        ctx = rng.integers(-3, stride * 16 + 40, 37).astype(np.int32)
+        ctx[:3] = [0, stride * 16, 1]
+        got = B.decode_plan(pool, ctx, stride)
+        assert got.tolist() == expected_plan(ctx, stride)
+        cap = L.pa_decode_plan_capacity(h, len(ctx), stride)
+        assert cap == len(ctx) * ((stride + 63) // 64)
+        assert len(got) <= cap
+    L.pa_pool_destroy(h)
+
+
+def test_plan_validation():
+    import numpy as np
+    L = B.lib()
+    h = make_pool(d=128)
+    n = ctypes.c_int32(-1)
+    ctx = np.array([100, 5000, 0], dtype=np.int32)
+    buf = np.zeros(8, dtype=np.int32)
+    assert L.pa_decode_plan_capacity(None, 3, 10) == -1
+    assert L.pa_decode_plan_capacity(h, 3, 0) == -1
+    assert L.pa_decode_plan_capacity(h, (1 << 20) + 1, 10) == -1
+    assert L.pa_decode_plan_capacity(h, 1, 64 * 2048 + 1) == -1
+    assert L.pa_decode_plan(h, ctx.ctypes.data, 3, 400, buf.ctypes.data, 8, None) == NULL
+    assert L.pa_decode_plan(h, None, 3, 400, buf.ctypes.data, 8, ctypes.byref(n)) == NULL
+    assert L.pa_decode_plan(h, ctx.ctypes.data, 3, 400, None, 8, ctypes.byref(n)) == NULL
+    # 5000 tokens = 313 pages = 5 splits; +1 for 100 tokens, +1 for the empty context
+    assert L.pa_decode_plan(h, ctx.ctypes.data, 3, 400, buf.ctypes.data, 6, ctypes.byref(n)) == INVALID
+    assert L.pa_decode_plan(h, ctx.ctypes.data, 3, 400, buf.ctypes.data, 8, ctypes.byref(n)) == OK
+    assert n.value == 7
+    assert buf[:7].tolist() == expected_plan(ctx, 400)
+    assert L.pa_decode_plan(h, ctx.ctypes.data, 0, 400, None, 0, ctypes.byref(n)) == OK and n.value == 0
+    L.pa_pool_destroy(h)
+
+
+def test_planned_decode_validation():
+    L = B.lib()
+    h = make_pool(d=64)
+    ws = 1 << 24
+
+    def call(plan=P, items=4, num_seqs=2, stride=70, ws_ptr=P, ws_bytes=ws):
+        return L.pa_decode_planned(h, P, num_seqs, 32, P, stride, P, 0.125, P2, ws_ptr, ws_bytes, plan,
+                                   items, None)
+
+    assert call(plan=None) == NULL
+    assert call(plan=P + 2) == ALIGN
+    assert call(items=-1) == INVALID
+    assert call(items=5) == INVALID          # 2 sequences x 2 splits at most
+    assert call(ws_ptr=None, ws_bytes=0) == WORKSPACE
+    assert call(num_seqs=0, plan=None, items=0) == OK
+    L.pa_pool_destroy(h)

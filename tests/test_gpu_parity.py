@@ -77,10 +77,14 @@ def test_c4_full_step_sampled():
     import torch
     dev = device()
     w = W.make_workload("c4")
-    log(f"c4: L=16 B=256 pages={w.num_pages} max_ctx={w.ctx_lens.max()} entry=pa_kv_append+pa_decode")
+    log(f"c4: L=16 B=256 pages={w.num_pages} max_ctx={w.ctx_lens.max()} entry=pa_kv_append+pa_decode_planned")
     up = Uploaded(w, dev)
-    out = up.step(fused=False).cpu().numpy()       # the two-call step the benchmark times
+    out = up.step(fused=False, planned=True).cpu().numpy()   # the step the benchmark times
     torch.cuda.synchronize()
+    # the plan changes only the launch order: pa_decode gives the same bits
+    for layer in (0, 15):
+        plain = B.decode(up.pool, up.q[layer], up.bt[layer], up.ctx, float(w.scale), workspace=up.workspace)
+        assert np.array_equal(plain.cpu().numpy(), out[layer]), f"c4 layer {layer}: planned != plain"
     rng = np.random.default_rng(3)
     order = np.argsort(w.ctx_lens, kind="stable")
     cases = [(0, int(order[-1])), (15, int(order[0])), (7, int(order[128]))]
@@ -128,6 +132,8 @@ def test_edge_cases(label, ctx, hq, hkv, d):
     out = up.step().cpu().numpy()
     ref = full_oracle(w, up)
     a, r = check_parity(out, ref, label)
+    planned = up.step(fused=False, planned=True).cpu().numpy()
+    assert np.array_equal(planned, out), f"{label}: pa_decode_planned differs from pa_decode"
     for b, n in enumerate(w.ctx_lens):
         if n == 0:
             assert np.array_equal(out[0, b], np.zeros_like(out[0, b])), "ctx 0 must give zeros"

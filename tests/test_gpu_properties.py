@@ -218,3 +218,36 @@ def test_stream_read_helper():
     B.stream_read(buf, sink)
     torch.cuda.synchronize()
     assert int(sink[0]) == 0
+
+
+@pytest.mark.parametrize("case", ["custom", "c3", "c5"])
+def test_planned_decode_is_bitwise_plain_decode(case):
+    import torch
+    dev = device()
+    if case == "custom":
+        ctx = [0, 1, 16, 17, 1024, 1025, 3000, 40, 2049, 0, 777]
+        w = W.custom(seed=21, ctx_lens=ctx, stride=200)
+    else:
+        w = W.make_workload(case)
+    log(f"planned decode vs pa_decode: {case}, {w.num_seqs} seqs, d={w.head_dim}")
+    up = Uploaded(w, dev)
+    plain = up.step().clone()
+    stride = w.block_tables.shape[-1]
+    plan_host = B.decode_plan(up.pool, w.ctx_lens, stride)
+    # items out of range are skipped on the device
+    s_max = -(-stride // (B.split_tokens(w.head_dim) // 16))
+    bogus = np.array([w.num_seqs + 5, (s_max << 20) | 0], dtype=np.int32)
+    for extra in (np.zeros(0, np.int32), bogus):
+        p = np.concatenate([plan_host, extra])
+        if p.size > B.lib().pa_decode_plan_capacity(up.pool.handle, w.num_seqs, stride):
+            continue
+        plan = torch.from_numpy(p).to(dev)
+        out = torch.full_like(plain[0], float("nan"))
+        B.decode_planned(up.pool, up.q[0], up.bt[0], up.ctx, float(w.scale), plan, out=out,
+                         workspace=up.workspace)
+        torch.cuda.synchronize()
+        assert bool((out == plain[0]).all()), f"{case}: planned decode differs from pa_decode"
+    if case == "custom":
+        ref = oracle.decode_attention(up.q_host[0], w.pool_bits("k"), w.pool_bits("v"),
+                                      w.block_tables[0], w.ctx_lens, w.scale)
+        check_parity(out.cpu().numpy(), ref, "planned decode vs oracle")
