@@ -24,8 +24,9 @@
 //     through the MFMA, so the weights keep ~16 significant bits.
 //
 // Every K/V byte is loaded once, 16 bytes per lane per load, straight into the
-// registers of its MFMA operand; the next pair's loads are issued before the
-// current pair is computed. Waves merge (m, l, acc) through LDS; a split that
+// registers of its MFMA operand, with the nontemporal (streaming) hint where
+// it measured faster; the next pair's loads are issued before the current
+// pair is computed. Waves merge (m, l, acc) through LDS; a split that
 // is not alone writes its partial to the workspace and merge_splits combines
 // the splits of a sequence by log-sum-exp in split order.
 //
@@ -101,6 +102,26 @@ __device__ __forceinline__ int clamp_ctx(int n, int stride) {
   return n < 0 ? 0 : (n > stride * kPage ? stride * kPage : n);
 }
 
+// K/V pages are read once per launch: they are loaded with the nontemporal
+// hint (streaming cache policy), measured faster for d = 64 (K and V) and for
+// the V tiles of d = 128; the d = 128 K loads, whose 16-byte pieces of a
+// 128-byte line come from four instructions, measured slower with it.
+template <int D>
+__host__ __device__ constexpr bool nt_k() { return D == 64; }
+template <int D>
+__host__ __device__ constexpr bool nt_v() { return true; }
+
+// Head dims held by lane group grp for QK k-step kk (8 consecutive dims);
+// the keys (A operand), the query (B operand) and the fused append use it.
+template <int D>
+__host__ __device__ constexpr int kdim(int grp, int kk) { return (D / 4) * grp + 8 * kk; }
+
+template <bool NT>
+__device__ __forceinline__ u32x4 ld_stream(const u32x4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
 template <int D>
 struct PairBuf {
   u32x4 k[2][D / 32];   // QK A operands: MFMA j, k-step kk
@@ -143,9 +164,9 @@ __device__ __forceinline__ void issue_pair(const SplitCtx<D>& c, PairBuf<D>& buf
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) buf.k[j][kk] = *(const u32x4*)(kp + 4 * j * D + 8 * kk);
+    for (int kk = 0; kk < KK; ++kk) buf.k[j][kk] = ld_stream<nt_k<D>()>((const u32x4*)(kp + 4 * j * D + kdim<D>(0, kk)));
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) buf.v[mt] = *(const u32x4*)(vp + mt * 16 * kPage);
+  for (int mt = 0; mt < MT; ++mt) buf.v[mt] = ld_stream<nt_v<D>()>((const u32x4*)(vp + mt * 16 * kPage));
   // keep later pairs' loads and this pair's math in program order, so the
   // registers in use are the buffers as written
   __builtin_amdgcn_sched_barrier(0);
@@ -274,15 +295,15 @@ __device__ __forceinline__ void make_split_ctx(const DecodeArgs& a, int b, int k
   c.my_pid = lane < c.npages ? (raw_pid < 0 ? 0 : (raw_pid >= a.num_pages ? a.num_pages - 1 : raw_pid)) : 0;
   // query group as the MFMA B operand (columns = heads, zero past G)
   if (r < G) {
-    const uint16_t* qp = a.q + ((size_t)b * a.num_q_heads + (size_t)kvh * G + r) * D + (D / 4) * grp;
+    const uint16_t* qp = a.q + ((size_t)b * a.num_q_heads + (size_t)kvh * G + r) * D;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) c.qf[kk] = as_bf16x8(*(const u32x4*)(qp + 8 * kk));
+    for (int kk = 0; kk < KK; ++kk) c.qf[kk] = as_bf16x8(*(const u32x4*)(qp + kdim<D>(grp, kk)));
   } else {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) c.qf[kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   }
   c.page_elems = (size_t)a.num_kv_heads * TILE;
-  const int koff = (8 * ((r >> 2) & 1) + (r & 3)) * D + (D / 4) * grp;
+  const int koff = (8 * ((r >> 2) & 1) + (r & 3)) * D + kdim<D>(grp, 0);
   const int voff = r * kPage + 8 * (grp & 1);
   c.k_second = (r >> 3) != 0;
   c.v_second = (grp >> 1) != 0;
@@ -362,10 +383,10 @@ __device__ __forceinline__ void append_by_reader(const DecodeArgs& a, int b, int
   const uint16_t* vn = a.v_new + ((size_t)b * a.num_kv_heads + kvh) * D;
   // K: the QK row of this token is r = 8 * page-in-pair + 4 * (slot / 8) + slot % 4
   if (r == 8 * p_in_pair + 4 * (slot >> 3) + (slot & 3)) {
-    uint16_t* kdst = const_cast<uint16_t*>(a.kpool) + (tile * kPage + slot) * D + (D / 4) * grp;
+    uint16_t* kdst = const_cast<uint16_t*>(a.kpool) + (tile * kPage + slot) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      *(u32x4*)(kdst + 8 * kk) = *(const u32x4*)(kn + (D / 4) * grp + 8 * kk);
+      *(u32x4*)(kdst + kdim<D>(grp, kk)) = *(const u32x4*)(kn + kdim<D>(grp, kk));
   }
   // V: the two lane groups 2 * page-in-pair and 2 * page-in-pair + 1 load the
   // two 16-byte halves of every 32-byte slot row of this page. They read their
@@ -624,7 +645,7 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
   for (; i + 7 * stride < n16; i += 8 * stride) {
     u32x4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = p[i + u * stride];
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
 #pragma unroll
     for (int u = 0; u < 8; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
