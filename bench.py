@@ -3,13 +3,16 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4]
 
 A step is one pass of the whole path over one batch: for the default workload
-(16 layers, 256 sequences, lognormal contexts, 32q/8kv, d=64) that is, per
-layer, the paged append of the new token's K/V then paged decode attention
-(split kernel + merge kernel). Inputs are resident in HBM before timing.
-Prints one JSON line: achieved KV-read GB/s over the timed steps, the
+(16 layers, 256 sequences, lognormal contexts, 32q/8kv, d=64) that is the
+launch plan made on the host and copied to the device, then per layer the
+paged append of the new token's K/V and paged decode attention (split kernel
++ merge kernel), launched from Python (--graph replays them from a HIP graph
+captured once per input replica instead). Inputs are resident in HBM before
+timing. Prints one JSON line: achieved KV-read GB/s over the timed steps, the
 roofline of the dominant kernel (the decode split kernel, timed with HIP
-events on its own stream inside the timed region), and a CPU baseline (the
-FP64 oracle on a bounded sample of the same workload, on the host cores).
+events on the launch stream in a second, eager pass over the same steps),
+and a CPU baseline (the FP64 oracle on a bounded sample of the same workload,
+on the host cores).
 """
 
 from __future__ import annotations
@@ -61,6 +64,9 @@ def parse():
                     help="budget of timed oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step's launches from a HIP graph captured once per replica "
+                         "(default: launch from Python; measured faster on this stack)")
     return ap.parse_args()
 
 
@@ -89,19 +95,18 @@ class Inputs:
         self.plan_copied = [None, None]
         self.plan_dev = torch.empty(cap, dtype=torch.int32, device=dev)
         self.step_no = 0
+        self.graph = None
+        self.graph_items = -1
         need = B.decode_workspace_bytes(self.pool, w.num_seqs, w.num_q_heads, w.stride)
         self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
         self.out = torch.empty((w.num_layers, w.num_seqs, w.num_q_heads, w.head_dim),
                                dtype=torch.float32, device=dev)
 
 
-def run_step(w, x, B, stream):
-    """One step: the launch plan for this step's context lengths (host, then an
-    async copy to the device), then per layer the paged append of the new
-    token's K/V (pa_kv_append) and paged decode attention driven by the plan
-    (pa_decode_planned, bit-identical to pa_decode). The single-launch
-    pa_decode_append gives bit-identical results but measures slower, so the
-    step uses the two calls."""
+def upload_plan(w, x, B, stream):
+    """The launch plan for this step's context lengths: made on the host into a
+    pinned buffer, copied to the device on the launch stream. Returns the
+    device view the decode launches read."""
     import torch
     k = x.step_no & 1
     x.step_no += 1
@@ -114,11 +119,45 @@ def run_step(w, x, B, stream):
         ev = torch.cuda.Event()
         ev.record(stream)
         x.plan_copied[k] = ev
+    return plan
+
+
+def run_layers(w, x, B, stream, plan):
+    """Per layer: the paged append of the new token's K/V (pa_kv_append), then
+    paged decode attention driven by the plan (pa_decode_planned,
+    bit-identical to pa_decode). The single-launch pa_decode_append gives
+    bit-identical results but measures slower, so the step uses the two calls."""
     for layer in range(w.num_layers):
         if w.append:
             B.kv_append(x.pool, x.k_new[layer], x.v_new[layer], x.bt[layer], x.pos, stream=stream)
         B.decode_planned(x.pool, x.q[layer], x.bt[layer], x.ctx, float(w.scale), plan,
                          out=x.out[layer], workspace=x.ws, stream=stream)
+
+
+def run_step(w, x, B, stream):
+    """One step: the launch plan, then every layer's launches (replayed from a
+    HIP graph when one was captured for this replica)."""
+    import torch
+    plan = upload_plan(w, x, B, stream)
+    if x.graph is not None and plan.numel() == x.graph_items:
+        with torch.cuda.stream(stream):
+            x.graph.replay()
+    else:
+        run_layers(w, x, B, stream, plan)
+
+
+def capture_step(w, x, B, stream):
+    """Capture one step's launches (all layers, no plan upload) into a HIP graph
+    through torch; the plan buffer is read at replay time, so a replay serves
+    any plan with the same number of items."""
+    import torch
+    plan = upload_plan(w, x, B, stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        run_layers(w, x, B, stream, plan)
+    torch.cuda.synchronize()
+    x.graph, x.graph_items = g, plan.numel()
 
 
 def stream_ceiling(B, dev, stream):
@@ -205,12 +244,11 @@ def main():
     w = W.make_workload(args.workload)
     stream = torch.cuda.Stream(device=dev)     # default priority
 
-    # Workloads whose pool fits the device cache rotate over replicas so that
-    # every timed step reads from HBM.
+    # Workloads whose per-step K/V fits the device cache twice over rotate over
+    # replicas, so that at least 4x the cache is touched between reuses.
     replicas = 1
-    if w.pool_bytes() * 2 < 2 * MALL_BYTES:
-        replicas = max(2, math.ceil(4 * MALL_BYTES / w.pool_bytes()))
-        replicas = min(replicas, 16)
+    if w.kv_bytes_per_step() < 2 * MALL_BYTES:
+        replicas = min(16, max(2, math.ceil(4 * MALL_BYTES / w.kv_bytes_per_step())))
     t0 = time.time()
     xs = [Inputs(w, dev, B) for _ in range(replicas)]
     torch.cuda.synchronize()
@@ -219,9 +257,16 @@ def main():
           f"inputs made in {gen_s:.1f} s", file=sys.stderr, flush=True)
 
     with torch.cuda.stream(stream):
-        for i in range(args.warmup):
+        for i in range(max(args.warmup, replicas)):
             run_step(w, xs[i % replicas], B, stream)
     torch.cuda.synchronize()
+    if args.graph:
+        for x in xs:
+            capture_step(w, x, B, stream)
+        with torch.cuda.stream(stream):
+            for i in range(replicas):
+                run_step(w, xs[i % replicas], B, stream)
+        torch.cuda.synchronize()
 
     # Timed region: K steps between two events on the launch stream.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -241,10 +286,12 @@ def main():
     # Kernel durations: the same K steps again with every kernel the library
     # queues bracketed by HIP events on the launch stream (the brackets add
     # small gaps between kernels, so the step time above is taken without them).
+    # This pass launches eagerly: graph replays bypass the library's brackets.
     B.profile_start()
     with torch.cuda.stream(stream):
         for i in range(args.steps):
-            run_step(w, xs[i % replicas], B, stream)
+            x = xs[i % replicas]
+            run_layers(w, x, B, stream, upload_plan(w, x, B, stream))
     torch.cuda.synchronize()
     prof = B.profile_stop()
 
@@ -298,6 +345,7 @@ def main():
             "kv_bytes_per_step": kv_step,
             "pool_pages": w.num_pages,
             "replicas": replicas,
+            "launch": "hip graph replay per step (plan copied before it)" if args.graph else "eager",
             "parallelism": "single GPU",
         },
         "roofline": {
