@@ -76,7 +76,9 @@ typedef enum pa_status {
   PA_ERR_UNSUPPORTED = 3, /* valid in principle, not built: head_dim, page size, group size */
   PA_ERR_ALIGN = 4,       /* a device pointer is not aligned as documented below */
   PA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than pa_decode_workspace_bytes */
-  PA_ERR_LAUNCH = 6       /* the HIP runtime reported an error when queueing a kernel */
+  PA_ERR_LAUNCH = 6,      /* the HIP runtime reported an error when queueing a kernel */
+  PA_ERR_CAPACITY = 7,    /* a request larger than the whole pool: rejected (pakv_sched.h) */
+  PA_ERR_STATE = 8        /* a request is not in a state that allows the call (pakv_sched.h) */
 } pa_status;
 
 /* Opaque host-side description of one K/V page pool (no device memory). */

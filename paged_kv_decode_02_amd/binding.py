@@ -18,12 +18,17 @@ LIB_PATH = os.path.join(HERE, "libpakv.so")
 
 PA_OK = 0
 PA_ERR_INVALID = 2
-STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_INVALID", 3: "PA_ERR_UNSUPPORTED",
+PA_ERR_CAPACITY = 7
+PA_ERR_STATE = 8
+STATUS_NAMES = {7: "PA_ERR_CAPACITY", 8: "PA_ERR_STATE",
+                0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_INVALID", 3: "PA_ERR_UNSUPPORTED",
                 4: "PA_ERR_ALIGN", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_LAUNCH"}
 EXPORTS = ["pa_pool_create", "pa_pool_destroy", "pa_kv_append", "pa_decode_workspace_bytes",
            "pa_split_tokens", "pa_decode", "pa_decode_append", "pa_status_str", "pa_profile_start",
            "pa_profile_stop", "pa_stream_read", "pa_decode_plan_capacity", "pa_decode_plan",
-           "pa_decode_planned"]
+           "pa_decode_planned", "pa_sched_create", "pa_sched_destroy", "pa_sched_submit",
+           "pa_sched_submit_shared", "pa_sched_admit", "pa_sched_slot", "pa_sched_advance",
+           "pa_sched_finish", "pa_sched_block_tables", "pa_sched_context_lens", "pa_sched_stats"]
 
 _lib = None
 
@@ -79,6 +84,30 @@ def lib() -> ctypes.CDLL:
                                     c.c_void_p, c.c_float, c.c_void_p, c.c_void_p, c.c_size_t,
                                     c.c_void_p, c.c_int32, c.c_void_p]
     L.pa_decode_planned.restype = c.c_int
+    i32p, i64p = c.POINTER(c.c_int32), c.POINTER(c.c_int64)
+    L.pa_sched_create.argtypes = [c.POINTER(c.c_void_p), c.c_int32, c.c_int32, c.c_int32, c.c_int32,
+                                  c.c_int32]
+    L.pa_sched_create.restype = c.c_int
+    L.pa_sched_destroy.argtypes = [c.c_void_p]
+    L.pa_sched_destroy.restype = None
+    L.pa_sched_submit.argtypes = [c.c_void_p, c.c_int32, c.c_int32, i64p]
+    L.pa_sched_submit.restype = c.c_int
+    L.pa_sched_submit_shared.argtypes = [c.c_void_p, c.c_int64, c.c_int32, c.c_int32, c.c_int32, i64p]
+    L.pa_sched_submit_shared.restype = c.c_int
+    L.pa_sched_admit.argtypes = [c.c_void_p, c.c_void_p, c.c_int32, i32p]
+    L.pa_sched_admit.restype = c.c_int
+    L.pa_sched_slot.argtypes = [c.c_void_p, c.c_int64, i32p]
+    L.pa_sched_slot.restype = c.c_int
+    L.pa_sched_advance.argtypes = [c.c_void_p, c.c_int64, c.c_int32]
+    L.pa_sched_advance.restype = c.c_int
+    L.pa_sched_finish.argtypes = [c.c_void_p, c.c_int64]
+    L.pa_sched_finish.restype = c.c_int
+    L.pa_sched_block_tables.argtypes = [c.c_void_p]
+    L.pa_sched_block_tables.restype = i32p
+    L.pa_sched_context_lens.argtypes = [c.c_void_p]
+    L.pa_sched_context_lens.restype = i32p
+    L.pa_sched_stats.argtypes = [c.c_void_p, i32p, i32p, i32p]
+    L.pa_sched_stats.restype = c.c_int
     _lib = L
     return L
 
@@ -300,3 +329,78 @@ def stream_read(src, sink, stream=None):
     """Read all of ``src`` with 16-byte loads (bandwidth ceiling measurement)."""
     nbytes = src.numel() * src.element_size()
     _check(lib().pa_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "pa_stream_read")
+
+
+PA_BATCH_CONTINUOUS = 0
+PA_BATCH_STATIC = 1
+
+
+class Scheduler:
+    """Host page allocator and FIFO admission over a shared page pool
+    (pakv_sched.h). ``block_tables`` / ``context_lens`` are numpy views of the
+    scheduler's own host arrays ([L][max_batch][max_pages_per_seq] and
+    [max_batch]); they change as requests are admitted, advanced and finished."""
+
+    def __init__(self, num_pages: int, num_layers: int, max_batch: int, max_pages_per_seq: int,
+                 mode: int = PA_BATCH_CONTINUOUS):
+        import numpy as np
+        h = ctypes.c_void_p()
+        _check(lib().pa_sched_create(ctypes.byref(h), num_pages, num_layers, max_batch,
+                                     max_pages_per_seq, mode), "pa_sched_create")
+        self.handle = h
+        self.num_pages, self.num_layers = num_pages, num_layers
+        self.max_batch, self.stride = max_batch, max_pages_per_seq
+        bt = lib().pa_sched_block_tables(h)
+        cl = lib().pa_sched_context_lens(h)
+        self.block_tables = np.ctypeslib.as_array(bt, shape=(num_layers, max_batch, max_pages_per_seq))
+        self.context_lens = np.ctypeslib.as_array(cl, shape=(max_batch,))
+
+    def submit(self, prompt_tokens: int, max_new_tokens: int) -> int:
+        rid = ctypes.c_int64(0)
+        _check(lib().pa_sched_submit(self.handle, prompt_tokens, max_new_tokens, ctypes.byref(rid)),
+               "pa_sched_submit")
+        return rid.value
+
+    def submit_shared(self, parent: int, shared_tokens: int, prompt_tokens: int,
+                      max_new_tokens: int) -> int:
+        rid = ctypes.c_int64(0)
+        _check(lib().pa_sched_submit_shared(self.handle, parent, shared_tokens, prompt_tokens,
+                                            max_new_tokens, ctypes.byref(rid)),
+               "pa_sched_submit_shared")
+        return rid.value
+
+    def admit(self, capacity: Optional[int] = None):
+        import numpy as np
+        cap = self.max_batch if capacity is None else capacity
+        out = np.zeros(max(cap, 1), dtype=np.int64)
+        n = ctypes.c_int32(0)
+        _check(lib().pa_sched_admit(self.handle, out.ctypes.data, cap, ctypes.byref(n)), "pa_sched_admit")
+        return [int(x) for x in out[:n.value]]
+
+    def slot(self, rid: int) -> int:
+        s = ctypes.c_int32(0)
+        _check(lib().pa_sched_slot(self.handle, rid, ctypes.byref(s)), "pa_sched_slot")
+        return s.value
+
+    def advance(self, rid: int, tokens: int = 1):
+        _check(lib().pa_sched_advance(self.handle, rid, tokens), "pa_sched_advance")
+
+    def finish(self, rid: int):
+        _check(lib().pa_sched_finish(self.handle, rid), "pa_sched_finish")
+
+    def stats(self):
+        f, q, r = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(lib().pa_sched_stats(self.handle, ctypes.byref(f), ctypes.byref(q), ctypes.byref(r)),
+               "pa_sched_stats")
+        return {"free_pages": f.value, "queued": q.value, "running": r.value}
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            lib().pa_sched_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -28,7 +28,8 @@ def hipcc() -> str:
 
 
 def build(out_path: str | None = None, defines=(), verbose: bool = False) -> str:
-    """Compile csrc/pakv.hip into a shared library; returns its path."""
+    """Compile csrc/pakv.hip (kernels and their host side) and csrc/pakv_sched.cpp
+    (host page allocator) into one shared library; returns its path."""
     out_path = out_path or os.path.join(HERE, LIB_NAME)
     tmp = out_path + ".tmp"
     cmd = [
@@ -41,6 +42,7 @@ def build(out_path: str | None = None, defines=(), verbose: bool = False) -> str
         f"-I{INCLUDE}", f"-I{CSRC}",
         *[f"-D{d}" for d in defines],
         os.path.join(CSRC, "pakv.hip"),
+        os.path.join(CSRC, "pakv_sched.cpp"),
         "-Wl,-rpath,/opt/rocm/lib",
         "-o", tmp,
     ]

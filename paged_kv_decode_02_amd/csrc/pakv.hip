@@ -151,6 +151,8 @@ const char* pa_status_str(pa_status s) {
     case PA_ERR_ALIGN: return "a device pointer is not aligned as documented";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_LAUNCH: return "the HIP runtime failed to queue a kernel";
+    case PA_ERR_CAPACITY: return "the request needs more pages than the whole pool: rejected";
+    case PA_ERR_STATE: return "the request is not in a state that allows this call";
   }
   return "unknown status";
 }

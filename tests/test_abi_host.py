@@ -20,7 +20,7 @@ MIS = 0x10008
 
 
 def header_functions():
-    text = open(HEADER).read()
+    text = "".join(open(os.path.join(ROOT, "include", f)).read() for f in sorted(os.listdir(os.path.join(ROOT, "include"))) if f.endswith(".h"))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
 
