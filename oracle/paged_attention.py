@@ -1,4 +1,6 @@
-"""Plain FP64 CPU oracle for paged decode attention and the paged KV append.
+"""Plain FP64 CPU oracle for paged decode attention, the paged KV append, and
+paged prefill attention (a chunk of prompt tokens written into the pages, then
+causal attention over them).
 
 TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, calls or links
 this module: only the tests, the smoke check and the benchmark's CPU-baseline
@@ -17,6 +19,9 @@ Sources (web pages, cited by title and section):
 * [samir-review] comrad404.com review of the samir-vllm README, section
   "Что README говорит о KV-кэше и пакетном декодировании": prefill fills a
   request's pages, decode adds the new token's K/V.
+* [tiny-vllm] ... section "Prefill vs. Decode": prefill processes all the
+  input tokens at once (compute-bound); decode produces one token at a time
+  (bound by fetching the cached K/V).
 * [tiny-vllm] "Construye tu propio motor de inferencia LLM de alto rendimiento
   en C++ y CUDA" (aibit.im), section "Atención de Consulta Agrupada (GQA)":
   contiguous grouping, q head i uses KV head i / (q heads per KV head), and a
@@ -157,3 +162,68 @@ def kv_append(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray,
             k_out[physical, g, slot, :] = k_new[b, g, :]
             v_out[physical, g, :, slot] = v_new[b, g, :]
     return k_out, v_out
+
+
+def kv_write(k_pool: np.ndarray, v_pool: np.ndarray, k_rows: np.ndarray,
+             v_rows: np.ndarray, query_start: np.ndarray, block_tables: np.ndarray,
+             ctx_before: np.ndarray):
+    """Write each sequence's chunk of new tokens into its pages.
+
+    Prefill fills a request's pages ([samir-review]). Sequence ``b`` owns rows
+    ``query_start[b] .. query_start[b+1]-1`` of ``k_rows``/``v_rows`` (uint16
+    ``[N][Hkv][d]``); its row ``i`` is the token at position
+    ``ctx_before[b] + i``, stored by the same rule as a single appended token
+    (slot ``pos % 16`` of page ``block_table[pos // 16]``). Returns new pools.
+    """
+    k_out = np.array(k_pool, dtype=np.uint16, copy=True)
+    v_out = np.array(v_pool, dtype=np.uint16, copy=True)
+    for b in range(len(query_start) - 1):
+        for row in range(int(query_start[b]), int(query_start[b + 1])):
+            pos = int(ctx_before[b]) + row - int(query_start[b])
+            physical = int(block_tables[b][pos // PAGE_SIZE])
+            slot = pos % PAGE_SIZE
+            k_out[physical, :, slot, :] = k_rows[row]
+            v_out[physical, :, :, slot] = v_rows[row]
+    return k_out, v_out
+
+
+def prefill_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+                      k_rows: np.ndarray, v_rows: np.ndarray, query_start: np.ndarray,
+                      block_tables: np.ndarray, ctx_before: np.ndarray, scale: float):
+    """Prefill of a chunk of new tokens per sequence, in float64.
+
+    Prefill processes all input tokens of a request at once ([tiny-vllm],
+    "Prefill vs. Decode") and fills the request's pages ([samir-review]).
+    Readings: attention is causal (the token at position ``p`` attends over
+    positions ``0 .. p`` of its own sequence, as in any decoder-only model;
+    the pages do not print the mask), and a chunk may continue a cache that
+    already holds ``ctx_before[b]`` tokens (a shared prefix, or an earlier
+    chunk).
+
+    q            uint16 ``[N][Hq][d]``, row ``query_start[b] + i`` is token ``i``
+                 of sequence ``b``'s chunk
+    k_rows/v_rows uint16 ``[N][Hkv][d]``, the chunk's keys and values
+    query_start  int ``[B + 1]``, nondecreasing row offsets
+    ctx_before   int ``[B]``, tokens already in each sequence's cache
+    returns      (out float64 ``[N][Hq][d]``, k_pool', v_pool') with the chunk
+                 written into the pools
+    """
+    k_new_pool, v_new_pool = kv_write(k_pool, v_pool, k_rows, v_rows, query_start,
+                                      block_tables, ctx_before)
+    num_rows, num_q_heads, head_dim = q.shape
+    group = num_q_heads // k_pool.shape[1]
+    scale = float(np.float64(scale))
+    out = np.zeros((num_rows, num_q_heads, head_dim), dtype=np.float64)
+    for b in range(len(query_start) - 1):
+        first, last = int(query_start[b]), int(query_start[b + 1])
+        if last == first:
+            continue
+        before = int(ctx_before[b])
+        kc, vc = gather_sequence(k_new_pool, v_new_pool, block_tables[b], before + last - first)
+        for row in range(first, last):
+            p = before + row - first                 # the query token's position
+            qr = bf16_bits_to_f64(q[row])
+            for h in range(num_q_heads):
+                g = h // group
+                out[row, h] = attend_one_head(qr[h], kc[:p + 1, g, :], vc[:p + 1, g, :], scale)
+    return out, k_new_pool, v_new_pool

@@ -356,9 +356,124 @@ def pin_append_then_gather(o):
     assert np.array_equal(v3 != v_pool, keep_v), "skipped sequence: V bits changed"
 
 
+# ------------------------------------------------------------ prefill pins
+def make_prefill_case(rng, hq, hkv, d, befores, chunks, extra_pages=4, sigma=1.0):
+    """Contiguous K/V for ``before + chunk`` tokens per sequence: the first
+    ``before`` tokens already in pages, the chunk's rows passed separately."""
+    tot = [int(a) + int(c) for a, c in zip(befores, chunks)]
+    kc = [random_bf16(rng, (n, hkv, d), sigma) for n in tot]
+    vc = [random_bf16(rng, (n, hkv, d), sigma) for n in tot]
+    q = random_bf16(rng, (int(sum(chunks)), hq, d), sigma)
+    per_seq = [max(1, -(-n // PAGE)) for n in tot]
+    k_pool, v_pool, bt = scatter_pages([k[:a] for k, a in zip(kc, befores)],
+                                       [v[:a] for v, a in zip(vc, befores)], befores,
+                                       sum(per_seq) + extra_pages, rng, pages_per_seq=per_seq)
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int64)
+    k_rows = np.concatenate([k[a:] for k, a in zip(kc, befores)]).astype(np.uint16)
+    v_rows = np.concatenate([v[a:] for v, a in zip(vc, befores)]).astype(np.uint16)
+    return q, kc, vc, k_pool, v_pool, bt, qs, np.asarray(befores, np.int64), k_rows, v_rows
+
+
+def pin_prefill_sdpa_library(o):
+    """Causal prefill equals torch's scaled_dot_product_attention in float64
+    on contiguous K/V: is_causal=True for an empty cache, and an explicit
+    mask (key j visible to chunk token i iff j <= before + i) otherwise."""
+    import torch
+    rng = np.random.default_rng(41)
+    for hq, hkv, d, befores, chunks in [(8, 2, 16, [0, 0], [1, 37]),
+                                        (6, 3, 8, [5, 16, 40], [20, 3, 17]),
+                                        (7, 1, 32, [0, 31], [33, 1])]:
+        q, kc, vc, k_pool, v_pool, bt, qs, bef, k_rows, v_rows = make_prefill_case(
+            rng, hq, hkv, d, befores, chunks)
+        scale = np.float32(1.0 / math.sqrt(d))
+        out, _, _ = o.prefill_attention(q, k_pool, v_pool, k_rows, v_rows, qs, bt, bef, scale)
+        g = hq // hkv
+        for b, (a, c) in enumerate(zip(befores, chunks)):
+            rows = slice(int(qs[b]), int(qs[b + 1]))
+            qt = torch.from_numpy(bits_to_f64_ref(q[rows])).permute(1, 0, 2).unsqueeze(0)   # [1][hq][c][d]
+            kt = torch.from_numpy(bits_to_f64_ref(kc[b])).permute(1, 0, 2).repeat_interleave(g, 0)
+            vt = torch.from_numpy(bits_to_f64_ref(vc[b])).permute(1, 0, 2).repeat_interleave(g, 0)
+            kt, vt = kt.unsqueeze(0).contiguous(), vt.unsqueeze(0).contiguous()
+            if a == 0:
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    qt.contiguous(), kt, vt, is_causal=True, scale=float(scale))
+            else:
+                mask = torch.arange(a + c)[None, :] <= (a + torch.arange(c))[:, None]
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    qt.contiguous(), kt, vt, attn_mask=mask, scale=float(scale))
+            _assert_close(out[rows], ref[0].permute(1, 0, 2).numpy(), 1e-12, f"prefill sdpa b={b}")
+
+
+def pin_prefill_last_row_is_decode(o):
+    """The last chunk token of every sequence sees the whole cache: its row is
+    decode attention over before + chunk tokens of the written pool."""
+    rng = np.random.default_rng(42)
+    q, kc, vc, k_pool, v_pool, bt, qs, bef, k_rows, v_rows = make_prefill_case(
+        rng, 8, 4, 16, [0, 9, 32], [5, 30, 1])
+    out, k2, v2 = o.prefill_attention(q, k_pool, v_pool, k_rows, v_rows, qs, bt, bef, 0.25)
+    last = qs[1:] - 1
+    ref = o.decode_attention(q[last], k2, v2, bt, bef + np.diff(qs), 0.25)
+    _assert_close(out[last], ref, 1e-12, "last prefill row vs decode")
+
+
+def pin_prefill_causality(o):
+    """Changing chunk token j's key and value changes rows j.. only; rows
+    before it keep every bit."""
+    rng = np.random.default_rng(43)
+    q, kc, vc, k_pool, v_pool, bt, qs, bef, k_rows, v_rows = make_prefill_case(
+        rng, 4, 2, 8, [7], [12])
+    base, _, _ = o.prefill_attention(q, k_pool, v_pool, k_rows, v_rows, qs, bt, bef, 0.5)
+    for j in (0, 5, 11):
+        k2, v2 = k_rows.copy(), v_rows.copy()
+        k2[j] = random_bf16(rng, k2[j].shape)
+        v2[j] = random_bf16(rng, v2[j].shape)
+        out, _, _ = o.prefill_attention(q, k_pool, v_pool, k2, v2, qs, bt, bef, 0.5)
+        assert np.array_equal(out[:j], base[:j]), f"rows before {j} changed"
+        assert not np.allclose(out[j:], base[j:]), f"rows from {j} did not change"
+
+
+def pin_prefill_write_matches_appends(o):
+    """Writing a chunk equals appending its tokens one position at a time, bit
+    for bit; nothing else in the pools changes."""
+    rng = np.random.default_rng(44)
+    q, kc, vc, k_pool, v_pool, bt, qs, bef, k_rows, v_rows = make_prefill_case(
+        rng, 4, 2, 8, [0, 14, 3], [20, 2, 0])
+    k_w, v_w = o.kv_write(k_pool, v_pool, k_rows, v_rows, qs, bt, bef)
+    k_a, v_a = k_pool.copy(), v_pool.copy()
+    chunks = np.diff(qs)
+    for i in range(int(chunks.max())):
+        pos = np.where(i < chunks, bef + i, -1).astype(np.int32)
+        rows = np.minimum(qs[:-1] + i, len(k_rows) - 1)
+        k_a, v_a = o.kv_append(k_a, v_a, k_rows[rows], v_rows[rows], bt, pos)
+    assert np.array_equal(k_w, k_a) and np.array_equal(v_w, v_a), "chunk write != appends"
+    written = 0
+    for b in range(len(chunks)):
+        for i in range(int(chunks[b])):
+            pos = int(bef[b]) + i
+            page = bt[b][pos // PAGE]
+            assert np.array_equal(k_w[page, :, pos % PAGE, :], k_rows[qs[b] + i])
+            assert np.array_equal(v_w[page, :, :, pos % PAGE], v_rows[qs[b] + i])
+            written += 1
+    changed = int(np.count_nonzero(np.any(k_w != k_pool, axis=-1)))
+    assert changed <= written * k_pool.shape[1], "bits outside the written slots changed"
+
+
+def pin_prefill_one_token_is_decode(o):
+    """A one-token chunk is one append then one decode step."""
+    rng = np.random.default_rng(45)
+    q, kc, vc, k_pool, v_pool, bt, qs, bef, k_rows, v_rows = make_prefill_case(
+        rng, 6, 2, 16, [0, 1, 16, 47], [1, 1, 1, 1])
+    out, k2, v2 = o.prefill_attention(q, k_pool, v_pool, k_rows, v_rows, qs, bt, bef, 0.3)
+    k3, v3 = o.kv_append(k_pool, v_pool, k_rows, v_rows, bt, bef.astype(np.int32))
+    assert np.array_equal(k2, k3) and np.array_equal(v2, v3)
+    _assert_close(out, o.decode_attention(q, k3, v3, bt, bef + 1, 0.3), 1e-12, "one-token prefill")
+
+
 ALL_PINS = [pin_bf16_widening, pin_sdpa_library, pin_ctx_one_returns_value,
             pin_ctx_two_sigmoid, pin_identical_keys_mean,
             pin_zero_query_or_scale_mean, pin_value_ones_convex, pin_hard_max,
             pin_ctx_zero_gives_zeros, pin_page_permutation_invariant,
             pin_tail_and_free_pages_ignored, pin_power_of_two_scale,
-            pin_kv_head_locality, pin_gather_roundtrip, pin_append_then_gather]
+            pin_kv_head_locality, pin_gather_roundtrip, pin_append_then_gather,
+            pin_prefill_sdpa_library, pin_prefill_last_row_is_decode, pin_prefill_causality,
+            pin_prefill_write_matches_appends, pin_prefill_one_token_is_decode]

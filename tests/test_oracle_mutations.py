@@ -17,7 +17,7 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                    "oracle", "paged_attention.py")
 
 MUTATIONS = {
-    "gqa_modulo_mapping": ("g = h // group", "g = h % num_kv_heads"),
+    "gqa_modulo_mapping": ("g = h // group\n            out[b, h]", "g = h % num_kv_heads\n            out[b, h]"),
     "page_slot_swapped": ("logical_page = t // PAGE_SIZE", "logical_page = t % PAGE_SIZE"),
     "slot_from_page": ("slot = t % PAGE_SIZE\n        physical", "slot = (t + 1) % PAGE_SIZE\n        physical"),
     "block_table_ignored": ("physical = int(block_table_row[logical_page])", "physical = logical_page"),
@@ -41,6 +41,16 @@ MUTATIONS = {
                           "if n == 0:\n            out[b] = 1.0\n            continue\n        kc, vc"),
     "off_by_one_ctx": ("kc, vc = gather_sequence(k_pool, v_pool, block_tables[b], n)",
                        "kc, vc = gather_sequence(k_pool, v_pool, block_tables[b], max(1, n - 1))"),
+    "prefill_not_causal": ("kc[:p + 1, g, :], vc[:p + 1, g, :]", "kc[:, g, :], vc[:, g, :]"),
+    "prefill_causal_off_by_one": ("kc[:p + 1, g, :], vc[:p + 1, g, :]", "kc[:p + 2, g, :], vc[:p + 2, g, :]"),
+    "prefill_ignores_cache": ("p = before + row - first", "p = row - first"),
+    "prefill_gqa_modulo": ("g = h // group\n                out[row, h]",
+                           "g = h % k_pool.shape[1]\n                out[row, h]"),
+    "write_ignores_cache": ("pos = int(ctx_before[b]) + row - int(query_start[b])",
+                            "pos = row - int(query_start[b])"),
+    "write_v_from_k": ("v_out[physical, :, :, slot] = v_rows[row]", "v_out[physical, :, :, slot] = k_rows[row]"),
+    "prefill_reads_old_pool": ("kc, vc = gather_sequence(k_new_pool, v_new_pool,",
+                               "kc, vc = gather_sequence(k_pool, v_pool,"),
 }
 
 
