@@ -201,6 +201,47 @@ pa_status pa_decode_planned(const pa_pool* pool, const void* q, int32_t num_seqs
                             size_t workspace_bytes, const int32_t* plan,
                             int32_t num_items, void* stream);
 
+/*
+ * Paged prefill. A chunk of new tokens per sequence: prefill fills a
+ * request's pages (samir-vllm README review, KV-cache section) and processes
+ * all of its tokens at once ("Construye tu propio motor de inferencia LLM
+ * ..." (aibit.im), section "Prefill vs. Decode").
+ *
+ * Rows: sequence b owns rows query_start[b] .. query_start[b+1]-1 of the row
+ * arrays (q: BF16 [num_rows][num_q_heads][head_dim]; k_rows, v_rows: BF16
+ * [num_rows][num_kv_heads][head_dim]; out: FP32 [num_rows][num_q_heads]
+ * [head_dim]). Its row i is the token at position context_lens[b] + i:
+ * context_lens gives the tokens already in the cache before the chunk (0 for
+ * a new request; the shared prefix, or earlier chunks, otherwise).
+ * query_start: int32 [num_seqs + 1], nondecreasing, device memory.
+ * max_chunk: a host-side bound on every chunk's length (the grid is sized
+ * from it; longer chunks are cut to it).
+ *
+ * pa_kv_write: writes every chunk token's K/V into its page slot (slot
+ * pos % 16 of page block_tables[b][pos / 16]), bit for bit, nothing else.
+ *
+ * pa_prefill: pa_kv_write, then causal grouped-query attention: the token at
+ * position p of sequence b attends over positions 0 .. p of that sequence
+ * (its own chunk and the cache before it), read in place from the pages;
+ * FP32 accumulation and online softmax as in pa_decode. out[row][h] is
+ * written for every chunk row. Both calls queue their kernels on `stream`.
+ *
+ * Preconditions as for pa_decode (page ids in the pool; positions within the
+ * block-table row). Row offsets and lengths are clamped on the device so a
+ * violation cannot touch memory outside the row arrays, the pool or the
+ * block-table row. Alignment: q, k_rows, v_rows, out 16 bytes; int32 arrays
+ * 4 bytes. num_seqs, num_rows or max_chunk == 0 queues nothing.
+ */
+pa_status pa_kv_write(const pa_pool* pool, const void* k_rows, const void* v_rows,
+                      int32_t num_seqs, int32_t num_rows, int32_t max_chunk,
+                      const int32_t* query_start, const int32_t* block_tables,
+                      int32_t max_pages_per_seq, const int32_t* context_lens, void* stream);
+pa_status pa_prefill(const pa_pool* pool, const void* q, const void* k_rows, const void* v_rows,
+                     int32_t num_seqs, int32_t num_q_heads, int32_t num_rows, int32_t max_chunk,
+                     const int32_t* query_start, const int32_t* block_tables,
+                     int32_t max_pages_per_seq, const int32_t* context_lens, float scale,
+                     float* out, void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* pa_status_str(pa_status status);
 

@@ -28,7 +28,8 @@ EXPORTS = ["pa_pool_create", "pa_pool_destroy", "pa_kv_append", "pa_decode_works
            "pa_profile_stop", "pa_stream_read", "pa_decode_plan_capacity", "pa_decode_plan",
            "pa_decode_planned", "pa_sched_create", "pa_sched_destroy", "pa_sched_submit",
            "pa_sched_submit_shared", "pa_sched_admit", "pa_sched_slot", "pa_sched_advance",
-           "pa_sched_finish", "pa_sched_block_tables", "pa_sched_context_lens", "pa_sched_stats"]
+           "pa_sched_finish", "pa_sched_block_tables", "pa_sched_context_lens", "pa_sched_stats",
+           "pa_kv_write", "pa_prefill"]
 
 _lib = None
 
@@ -108,6 +109,13 @@ def lib() -> ctypes.CDLL:
     L.pa_sched_context_lens.restype = i32p
     L.pa_sched_stats.argtypes = [c.c_void_p, i32p, i32p, i32p]
     L.pa_sched_stats.restype = c.c_int
+    L.pa_kv_write.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_int32, c.c_int32, c.c_int32,
+                              c.c_void_p, c.c_void_p, c.c_int32, c.c_void_p, c.c_void_p]
+    L.pa_kv_write.restype = c.c_int
+    L.pa_prefill.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_int32, c.c_int32,
+                             c.c_int32, c.c_int32, c.c_void_p, c.c_void_p, c.c_int32, c.c_void_p,
+                             c.c_float, c.c_void_p, c.c_void_p]
+    L.pa_prefill.restype = c.c_int
     _lib = L
     return L
 
@@ -287,6 +295,49 @@ def decode_planned(pool: Pool, q, block_tables, context_lens, scale: float, plan
     return out
 
 
+def _chunk_common(q_or_k, query_start, block_tables, context_lens, max_chunk):
+    import torch
+    _need(query_start, "query_start", (torch.int32,), 1)
+    _need(block_tables, "block_tables", (torch.int32,), 2)
+    _need(context_lens, "context_lens", (torch.int32,), 1)
+    num_seqs = block_tables.shape[0]
+    if query_start.numel() != num_seqs + 1 or context_lens.numel() != num_seqs:
+        raise ValueError("query_start must hold num_seqs + 1 offsets and context_lens num_seqs values")
+    return num_seqs, q_or_k.shape[0], block_tables.shape[1], int(max_chunk)
+
+
+def kv_write(pool: Pool, k_rows, v_rows, query_start, block_tables, context_lens, max_chunk: int,
+             stream=None):
+    """Write chunks of new tokens' K/V (``[N][Hkv][d]``) into their pages (pa_kv_write)."""
+    _need(k_rows, "k_rows", _bf16_types(), 3)
+    _need(v_rows, "v_rows", _bf16_types(), 3)
+    num_seqs, num_rows, stride, max_chunk = _chunk_common(k_rows, query_start, block_tables,
+                                                          context_lens, max_chunk)
+    _check(lib().pa_kv_write(pool.handle, _ptr(k_rows), _ptr(v_rows), num_seqs, num_rows, max_chunk,
+                             _ptr(query_start), _ptr(block_tables), stride, _ptr(context_lens),
+                             _stream(stream)), "pa_kv_write")
+
+
+def prefill(pool: Pool, q, k_rows, v_rows, query_start, block_tables, context_lens, scale: float,
+            max_chunk: int, out=None, stream=None):
+    """Paged prefill (pa_prefill): write the chunks' K/V, then causal attention for
+    every chunk row. Returns ``out`` (FP32 ``[N][Hq][d]``)."""
+    import torch
+    _need(q, "q", _bf16_types(), 3)
+    _need(k_rows, "k_rows", _bf16_types(), 3)
+    _need(v_rows, "v_rows", _bf16_types(), 3)
+    num_seqs, num_rows, stride, max_chunk = _chunk_common(q, query_start, block_tables, context_lens,
+                                                          max_chunk)
+    if out is None:
+        out = torch.empty(tuple(q.shape), dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,), 3)
+    _check(lib().pa_prefill(pool.handle, _ptr(q), _ptr(k_rows), _ptr(v_rows), num_seqs, q.shape[1],
+                            num_rows, max_chunk, _ptr(query_start), _ptr(block_tables), stride,
+                            _ptr(context_lens), float(scale), _ptr(out), _stream(stream)),
+           "pa_prefill")
+    return out
+
+
 def decode_append(pool: Pool, q, k_new, v_new, positions, block_tables, context_lens, scale: float,
                   out=None, workspace=None, stream=None):
     """Append each sequence's new token then decode, in one launch (pa_decode_append)."""
@@ -317,12 +368,15 @@ def profile_start():
     _check(lib().pa_profile_start(), "pa_profile_start")
 
 
+PROFILE_KINDS = ("decode", "merge", "append", "write", "prefill")
+
+
 def profile_stop():
-    """Returns {"decode": (ms, launches), "merge": (...), "append": (...)}."""
-    ms = (ctypes.c_double * 3)()
-    n = (ctypes.c_int64 * 3)()
+    """Returns {kind: (ms, launches)} for the kinds in PROFILE_KINDS."""
+    ms = (ctypes.c_double * len(PROFILE_KINDS))()
+    n = (ctypes.c_int64 * len(PROFILE_KINDS))()
     _check(lib().pa_profile_stop(ms, n), "pa_profile_stop")
-    return {"decode": (ms[0], n[0]), "merge": (ms[1], n[1]), "append": (ms[2], n[2])}
+    return {k: (ms[i], n[i]) for i, k in enumerate(PROFILE_KINDS)}
 
 
 def stream_read(src, sink, stream=None):

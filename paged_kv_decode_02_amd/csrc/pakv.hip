@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "pakv_kernels.h"
+#include "pakv_prefill.h"
 
 // Split geometry per head_dim: pages per split and wavefronts per workgroup.
 // Fixed per head_dim so that a sequence's result does not depend on the batch.
@@ -40,6 +41,7 @@ struct pa_pool {
 namespace {
 
 constexpr int kMaxGroup = 16;   // query heads per KV head: the 16 MFMA columns
+constexpr int kProfileKinds = 5;  // decode, merge, append, chunk write, prefill
 constexpr int64_t kPlanMaxSeqs = 1 << 20;   // plan items pack b in 20 bits
 constexpr int64_t kPlanMaxSplits = 1 << 11; // and the split in the 11 above them
 
@@ -377,6 +379,118 @@ pa_status pa_decode_append(const pa_pool* pool, const void* q, const void* k_new
                      0, stream);
 }
 
+// Shared validation of a chunked (prefill / chunk write) call.
+static pa_status check_chunk_args(const pa_pool* pool, int32_t num_seqs, int32_t num_rows,
+                                  int32_t max_chunk, const int32_t* query_start,
+                                  const int32_t* block_tables, int32_t max_pages_per_seq,
+                                  const int32_t* context_lens) {
+  if (!pool) return PA_ERR_NULL;
+  if (num_seqs < 0 || num_rows < 0 || max_chunk < 0 || max_pages_per_seq < 1) return PA_ERR_INVALID;
+  if (static_cast<int64_t>(max_pages_per_seq) * pakv::kPage > INT_MAX) return PA_ERR_INVALID;
+  if (num_seqs == 0 || num_rows == 0 || max_chunk == 0) return PA_OK;
+  if (!query_start || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (!aligned4(query_start) || !aligned4(block_tables) || !aligned4(context_lens)) return PA_ERR_ALIGN;
+  return PA_OK;
+}
+
+static pa_status launch_write(const pa_pool* pool, const void* k_rows, const void* v_rows,
+                              int32_t num_seqs, int32_t num_rows, int32_t max_chunk,
+                              const int32_t* query_start, const int32_t* block_tables,
+                              int32_t max_pages_per_seq, const int32_t* context_lens,
+                              hipStream_t s) {
+  pakv::WriteArgs a;
+  a.kpool = static_cast<uint16_t*>(pool->k);
+  a.vpool = static_cast<uint16_t*>(pool->v);
+  a.k_rows = static_cast<const uint16_t*>(k_rows);
+  a.v_rows = static_cast<const uint16_t*>(v_rows);
+  a.query_start = query_start;
+  a.block_tables = block_tables;
+  a.ctx_before = context_lens;
+  a.num_pages = pool->num_pages;
+  a.num_seqs = num_seqs;
+  a.num_rows = num_rows;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.stride = max_pages_per_seq;
+  a.max_chunk = max_chunk;
+  a.pages_per_seq = (max_chunk + pakv::kPage - 1) / pakv::kPage + 1;
+  const int64_t blocks = static_cast<int64_t>(num_seqs) * a.pages_per_seq;
+  if (blocks > INT_MAX) return PA_ERR_INVALID;
+  (void)hipGetLastError();
+  {
+    LaunchTimer t(3, s);
+    if (pool->head_dim == 64)
+      hipLaunchKernelGGL((pakv::kv_write_kernel<64>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((pakv::kv_write_kernel<128>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
+  }
+  if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+pa_status pa_kv_write(const pa_pool* pool, const void* k_rows, const void* v_rows, int32_t num_seqs,
+                      int32_t num_rows, int32_t max_chunk, const int32_t* query_start,
+                      const int32_t* block_tables, int32_t max_pages_per_seq,
+                      const int32_t* context_lens, void* stream) {
+  pa_status st = check_chunk_args(pool, num_seqs, num_rows, max_chunk, query_start, block_tables,
+                                  max_pages_per_seq, context_lens);
+  if (st != PA_OK || num_seqs == 0 || num_rows == 0 || max_chunk == 0) return st;
+  if (!k_rows || !v_rows) return PA_ERR_NULL;
+  if (!aligned16(k_rows) || !aligned16(v_rows)) return PA_ERR_ALIGN;
+  return launch_write(pool, k_rows, v_rows, num_seqs, num_rows, max_chunk, query_start, block_tables,
+                      max_pages_per_seq, context_lens, static_cast<hipStream_t>(stream));
+}
+
+pa_status pa_prefill(const pa_pool* pool, const void* q, const void* k_rows, const void* v_rows,
+                     int32_t num_seqs, int32_t num_q_heads, int32_t num_rows, int32_t max_chunk,
+                     const int32_t* query_start, const int32_t* block_tables,
+                     int32_t max_pages_per_seq, const int32_t* context_lens, float scale,
+                     float* out, void* stream) {
+  pa_status st = check_chunk_args(pool, num_seqs, num_rows, max_chunk, query_start, block_tables,
+                                  max_pages_per_seq, context_lens);
+  if (st != PA_OK) return st;
+  if (num_q_heads < 1 || num_q_heads % pool->num_kv_heads != 0) return PA_ERR_INVALID;
+  if (!std::isfinite(scale)) return PA_ERR_INVALID;
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (group > kMaxGroup) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_rows == 0 || max_chunk == 0) return PA_OK;
+  if (!q || !k_rows || !v_rows || !out) return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_rows) || !aligned16(v_rows) || !aligned16(out)) return PA_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launch_write(pool, k_rows, v_rows, num_seqs, num_rows, max_chunk, query_start, block_tables,
+                    max_pages_per_seq, context_lens, s);
+  if (st != PA_OK) return st;
+  pakv::PrefillArgs a;
+  a.kpool = static_cast<const uint16_t*>(pool->k);
+  a.vpool = static_cast<const uint16_t*>(pool->v);
+  a.q = static_cast<const uint16_t*>(q);
+  a.query_start = query_start;
+  a.block_tables = block_tables;
+  a.ctx_before = context_lens;
+  a.out = out;
+  a.num_pages = pool->num_pages;
+  a.num_seqs = num_seqs;
+  a.num_rows = num_rows;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.group = group;
+  a.stride = max_pages_per_seq;
+  a.max_chunk = max_chunk;
+  a.row_blocks = static_cast<int32_t>((static_cast<int64_t>(max_chunk) * group + 63) / 64);
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  const int64_t blocks = static_cast<int64_t>(pool->num_kv_heads) * num_seqs * a.row_blocks;
+  if (blocks > INT_MAX) return PA_ERR_INVALID;
+  (void)hipGetLastError();
+  {
+    LaunchTimer t(4, s);
+    if (pool->head_dim == 64)
+      hipLaunchKernelGGL((pakv::prefill_kernel<64>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((pakv::prefill_kernel<128>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
+  }
+  if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
 pa_status pa_profile_start(void) {
   for (auto& r : g_records) {
     g_free_events.push_back(r.start);
@@ -390,7 +504,7 @@ pa_status pa_profile_start(void) {
 pa_status pa_profile_stop(double* ms, int64_t* launches) {
   if (!ms || !launches) return PA_ERR_NULL;
   g_profiling = false;
-  for (int k = 0; k < 3; ++k) {
+  for (int k = 0; k < kProfileKinds; ++k) {
     ms[k] = 0.0;
     launches[k] = 0;
   }

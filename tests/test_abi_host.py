@@ -147,12 +147,13 @@ def test_append_validation():
 def test_profile_and_status_strings():
     L = B.lib()
     assert L.pa_profile_start() == OK
-    ms = (ctypes.c_double * 3)()
-    n = (ctypes.c_int64 * 3)()
-    assert L.pa_profile_stop(ms, n) == OK and list(n) == [0, 0, 0]
+    kinds = len(B.PROFILE_KINDS)
+    ms = (ctypes.c_double * kinds)()
+    n = (ctypes.c_int64 * kinds)()
+    assert L.pa_profile_stop(ms, n) == OK and list(n) == [0] * kinds
     assert L.pa_profile_stop(None, n) == NULL
-    for s in range(7):
-        assert B.status_str(s)
+    for s in range(9):
+        assert B.status_str(s) and B.status_str(s) != "unknown status"
     assert L.pa_stream_read(P, 15, P2, None) == INVALID
     assert L.pa_stream_read(0, 16, P2, None) == NULL
 
@@ -230,4 +231,34 @@ def test_planned_decode_validation():
     assert call(items=5) == INVALID          # 2 sequences x 2 splits at most
     assert call(ws_ptr=None, ws_bytes=0) == WORKSPACE
     assert call(num_seqs=0, plan=None, items=0) == OK
+    L.pa_pool_destroy(h)
+
+
+def test_prefill_and_write_validation():
+    L = B.lib()
+    h = make_pool(d=64)
+
+    def pre(q=P, kr=P, vr=P, num_seqs=2, hq=32, rows=10, max_chunk=8, qs=P, bt=P, stride=4, ctx=P,
+            scale=0.125, out=P2):
+        return L.pa_prefill(h, q, kr, vr, num_seqs, hq, rows, max_chunk, qs, bt, stride, ctx, scale, out,
+                            None)
+
+    assert pre(q=None) == NULL
+    assert pre(out=None) == NULL
+    assert pre(qs=None) == NULL
+    assert pre(q=MIS) == ALIGN
+    assert pre(qs=P + 2) == ALIGN
+    assert pre(hq=12) == INVALID              # not a multiple of 8 KV heads
+    assert pre(hq=8 * 17) == UNSUPPORTED      # 17 query heads per KV head
+    assert pre(rows=-1) == INVALID
+    assert pre(max_chunk=-1) == INVALID
+    assert pre(stride=0) == INVALID
+    assert pre(scale=float("nan")) == INVALID
+    assert pre(num_seqs=0, q=None, qs=None) == OK
+    assert pre(max_chunk=0, q=None) == OK
+    assert L.pa_prefill(None, P, P, P, 1, 32, 1, 1, P, P, 1, P, 0.1, P2, None) == NULL
+    assert L.pa_kv_write(h, None, P, 1, 4, 4, P, P, 2, P, None) == NULL
+    assert L.pa_kv_write(h, MIS, P, 1, 4, 4, P, P, 2, P, None) == ALIGN
+    assert L.pa_kv_write(h, P, P, 1, 4, 4, P, P, 0, P, None) == INVALID
+    assert L.pa_kv_write(h, None, None, 0, 4, 4, None, None, 2, None, None) == OK
     L.pa_pool_destroy(h)
