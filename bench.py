@@ -32,21 +32,24 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E peak
 MALL_BYTES = 256 << 20   # device last-level (Infinity) cache
 PROFILE = os.path.join(ROOT, "profiles", "decode_split_kernel_c4.md")
+PREFILL_PROFILE = os.path.join(ROOT, "profiles", "prefill_kernel_prefill.md")
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense BF16 matrix-core peak
 KERNEL_SOURCES = ("paged_kv_decode_02_amd/csrc/pakv_kernels.h", "paged_kv_decode_02_amd/csrc/pakv.hip")
+PREFILL_SOURCES = KERNEL_SOURCES + ("paged_kv_decode_02_amd/csrc/pakv_prefill.h",)
 
 
-def counted_traffic(workload):
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
-    only if it was taken on this workload with the kernel sources as they are
-    now (sha256 of the sources); None otherwise."""
+def counted_traffic(workload, profile=PROFILE, profiled_workload="c4", sources=KERNEL_SOURCES):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, only if
+    it was taken on this workload with the kernel sources as they are now
+    (sha256 of the sources); None otherwise."""
     import hashlib
-    if workload != "c4" or not os.path.exists(PROFILE):
+    if workload != profiled_workload or not os.path.exists(profile):
         return None
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
-    for line in open(PROFILE):
+    for line in open(profile):
         if line.startswith("traffic_json:"):
             t = json.loads(line.split(":", 1)[1])
             if t.get("source_sha256") == h.hexdigest():
@@ -59,7 +62,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c4", choices=["tiny", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c4",
+                    choices=["tiny", "c2", "c3", "c4", "c5", "prefill", "prefill_d128", "prefill_chunked"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of timed oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -226,12 +230,196 @@ def cpu_baseline(w, budget_s):
             "us_per_step_extrapolated": round(t_oracle / nbytes * w.kv_bytes_per_step() * 1e6, 1)}
 
 
+# ------------------------------------------------------------------ prefill
+PREFILL_NAMES = {
+    "prefill": "16-layer prefill of 8 prompts x 2048 tokens, 32q/8kv d64, empty caches",
+    "prefill_d128": "prefill of 4 prompts x 4096 tokens, 28q/4kv d128, one layer, empty caches",
+    "prefill_chunked": "512-token chunks continuing 8 caches of U[0,4096] tokens, 32q/8kv d64, one layer",
+}
+
+
+class PrefillInputs:
+    def __init__(self, w, dev, B):
+        import torch
+        base = w.base
+        self.k = base.pool_device("k", dev)
+        self.v = base.pool_device("v", dev)
+        self.pool = B.Pool(self.k, self.v)
+        self.bt = torch.from_numpy(np.ascontiguousarray(base.block_tables)).to(dev)
+        self.qs = torch.from_numpy(w.query_start).to(dev)
+        self.before = torch.from_numpy(w.ctx_before).to(dev)
+        self.q = w.rows_device("q", dev)
+        self.k_rows = w.rows_device("k", dev)
+        self.v_rows = w.rows_device("v", dev)
+        self.out = torch.empty((base.num_layers, w.num_rows, base.num_q_heads, base.head_dim),
+                               dtype=torch.float32, device=dev)
+        self.max_chunk = int(w.chunks.max())
+
+
+def run_prefill_step(w, x, B, stream):
+    """One step: per layer, pa_prefill (the chunk's K/V written into the pages,
+    then causal attention for every chunk token)."""
+    for layer in range(w.base.num_layers):
+        B.prefill(x.pool, x.q[layer], x.k_rows[layer], x.v_rows[layer], x.qs, x.bt[layer], x.before,
+                  float(w.base.scale), x.max_chunk, out=x.out[layer], stream=stream)
+
+
+def prefill_cpu_baseline(w, budget_s):
+    """The FP64 oracle on random (layer, sequence, chunk row) units of the same
+    workload for about budget_s seconds: each row attends over its causal
+    prefix, gathered from pages that hold the cache and the written chunk
+    (regeneration and the chunk write are not timed)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    base = w.base
+    rng = np.random.default_rng(2025)
+    qs = w.query_start
+    g = base.num_q_heads // base.num_kv_heads
+    t_oracle, flops, rows_done = 0.0, 0, 0
+    while t_oracle < budget_s:
+        layer = int(rng.integers(base.num_layers))
+        b = int(rng.integers(len(w.chunks)))
+        n_tot = int(w.ctx_before[b]) + int(w.chunks[b])
+        pages = base.block_tables[layer, b, :-(-n_tot // 16)]
+        kp = base.pool_pages_bits("k", pages)
+        vp = base.pool_pages_bits("v", pages)
+        rows = np.arange(qs[b], qs[b + 1])
+        bt = np.arange(pages.size, dtype=np.int32)[None, :]
+        kp, vp = oracle.kv_write(kp, vp, w.rows_bits("k", layer, rows), w.rows_bits("v", layer, rows),
+                                 np.array([0, rows.size]), bt, np.array([w.ctx_before[b]]))
+        pick = rng.integers(0, rows.size, 16)
+        qsel = w.rows_bits("q", layer, rows[pick])
+        t0 = time.perf_counter()
+        kc, vc = oracle.gather_sequence(kp, vp, bt[0], n_tot)
+        for j, i in enumerate(pick):
+            p = int(w.ctx_before[b]) + int(i)
+            qr = oracle.bf16_bits_to_f64(qsel[j])
+            for h in range(base.num_q_heads):
+                oracle.attend_one_head(qr[h], kc[:p + 1, h // g], vc[:p + 1, h // g], float(base.scale))
+            flops += 4 * base.head_dim * base.num_q_heads * (p + 1)
+            rows_done += 1
+        t_oracle += time.perf_counter() - t0
+    if limiter is not None and hasattr(limiter, "unregister"):
+        limiter.unregister()
+    return {"value": round(flops / t_oracle / 1e12, 9), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows_done} random chunk rows (all query heads each) of random (layer, sequence) "
+                      f"units, {flops / 1e9:.2f} GFLOP in {t_oracle:.1f} s of oracle time (gather "
+                      f"included); BLAS limited to 1 thread"}
+
+
+def prefill_main(args):
+    import torch
+    from paged_kv_decode_02_amd import binding as B
+    from paged_kv_decode_02_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    B.lib()
+    w = W.make_prefill_workload(args.workload)
+    base = w.base
+    stream = torch.cuda.Stream(device=dev)
+    t0 = time.time()
+    x = PrefillInputs(w, dev, B)
+    torch.cuda.synchronize()
+    print(f"[bench] {w.name}: {w.num_rows} chunk rows x {base.num_layers} layer(s), pool "
+          f"{base.pool_bytes() / 1e9:.2f} GB, inputs made in {time.time() - t0:.1f} s",
+          file=sys.stderr, flush=True)
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            run_prefill_step(w, x, B, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(args.steps):
+            run_prefill_step(w, x, B, stream)
+        e1.record(stream)
+    e1.synchronize()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    flops_step = w.flops_per_layer() * base.num_layers
+    value = flops_step / (ms_step * 1e-3) / 1e12
+
+    B.profile_start()
+    with torch.cuda.stream(stream):
+        for _ in range(args.steps):
+            run_prefill_step(w, x, B, stream)
+    torch.cuda.synchronize()
+    prof = B.profile_stop()
+    pre_ms, pre_n = prof["prefill"]
+    wr_ms, wr_n = prof["write"]
+    pre_avg = pre_ms / max(pre_n, 1)
+    achieved = w.flops_per_layer() / (pre_avg * 1e-3) / 1e12
+    print(f"[bench] step {ms_step * 1e3:.1f} us; prefill kernel avg {pre_avg * 1e3:.1f} us x {pre_n}, "
+          f"chunk write {wr_ms / max(wr_n, 1) * 1e3:.1f} us x {wr_n}", file=sys.stderr, flush=True)
+    ceiling = ceiling_median = None
+    if not args.no_ceiling:
+        ceiling, ceiling_median = stream_ceiling(B, dev, stream)
+    cpu = None if args.no_cpu_baseline else prefill_cpu_baseline(w, args.cpu_seconds)
+    traffic = counted_traffic(w.name, PREFILL_PROFILE, "prefill", PREFILL_SOURCES)
+    result = {
+        "metric": "paged prefill attention: achieved TFLOP/s (% of BF16 matrix-core peak) + us/step",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "us_per_step": round(ms_step * 1e3, 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": PREFILL_NAMES[w.name],
+            "global_batch": int(len(w.chunks)),
+            "layers": base.num_layers,
+            "q_heads": base.num_q_heads,
+            "kv_heads": base.num_kv_heads,
+            "head_dim": base.head_dim,
+            "chunk_rows": w.num_rows,
+            "cache_before_mean": round(float(w.ctx_before.mean()), 1),
+            "flops_per_step": flops_step,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "prefill_kernel",
+            "achieved": round(achieved, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic["traffic_bytes_per_launch"] if traffic else None,
+            "avg_launch_us": round(pre_avg * 1e3, 2),
+            "algorithmic_flops_per_launch": w.flops_per_layer(),
+            "note": "algorithmic flops: 4 d per (query head, causal pair); the kernel also runs the "
+                    "P low half through the matrix cores and whole 32-key pairs past the diagonal",
+        },
+        "kernels_us_per_step": {"prefill": round(pre_ms / args.steps * 1e3, 1),
+                                "chunk_write": round(wr_ms / args.steps * 1e3, 1),
+                                "note": "separate profiled pass; each kernel bracketed by HIP events"},
+        "stream_read_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path runs on a "
               f"single MI355X and has no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload.startswith("prefill"):
+        prefill_main(args)
+        return
 
     import torch
     from paged_kv_decode_02_amd import binding as B

@@ -475,7 +475,8 @@ pa_status pa_prefill(const pa_pool* pool, const void* q, const void* k_rows, con
   a.group = group;
   a.stride = max_pages_per_seq;
   a.max_chunk = max_chunk;
-  a.row_blocks = static_cast<int32_t>((static_cast<int64_t>(max_chunk) * group + 63) / 64);
+  const int block_rows = pool->head_dim == 64 ? pakv::prefill_block_rows<64>() : pakv::prefill_block_rows<128>();
+  a.row_blocks = static_cast<int32_t>((static_cast<int64_t>(max_chunk) * group + block_rows - 1) / block_rows);
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   const int64_t blocks = static_cast<int64_t>(pool->num_kv_heads) * num_seqs * a.row_blocks;
   if (blocks > INT_MAX) return PA_ERR_INVALID;

@@ -14,19 +14,23 @@
 // Attention work decomposition. For one (sequence, KV head) the chunk's
 // query rows are the (token, head) pairs of the G query heads of that KV
 // head, row index rho = token * G + head. A workgroup of 4 wavefronts takes
-// 64 consecutive rows, 16 per wave; each wave streams the key pages its rows
-// can see (up to the position of its last token), two pages per step:
+// 128 consecutive rows, 32 per wave in two groups of 16; each wave streams
+// the key pages its rows can see (up to the position of its last token), two
+// pages per step, and every K/V operand it loads feeds both row groups:
 //
-//   S^T = K Q^T on the matrix cores (v_mfma_f32_16x16x32_bf16): A = the 16
-//     keys of a page x 32 head dims, B = 32 head dims x the wave's 16 rows;
-//     lane (r = lane % 16, grp = lane / 16) gets keys 4 grp + 0..3 of row r;
+//   S^T = K Q^T on the matrix cores (v_mfma_f32_16x16x32_bf16): A = 16 keys
+//     x 32 head dims, B = 32 head dims x one group's 16 rows. The 16 A rows
+//     of MFMA j mix the two pages (row r is page r / 8, slot
+//     8 ((r / 4) % 2) + 4 j + r % 4), so that lane (r = lane % 16,
+//     grp = lane / 16) ends up with slots 8 (grp % 2) + 0..7 of page grp / 2
+//     for row r: 8 consecutive keys, positions 32 pair + 8 grp + 0..7;
 //   causal mask by select, FP32 online softmax per row (the 4 lanes holding a
 //     row reduce their maxima with two xor shuffles);
-//   O^T += V^T P^T on the matrix cores: A = V^T (16 head dims x 32 keys: for
-//     lane group grp, keys 4 grp + 0..3 of each of the two pages, which are
-//     8 contiguous bytes of a slot-minor V row), B = P^T in the same key
-//     order, P split into BF16 hi + lo as in decode.
-// The waves share nothing; there is no LDS and no barrier.
+//   O^T += V^T P^T on the matrix cores: A = V^T (16 head dims x those 8 keys
+//     per lane group: one 16-byte load from the slot-minor V row), B = P^T,
+//     P split into BF16 hi + lo as in decode.
+// The waves share nothing; there is no LDS and no barrier. The row blocks
+// that see the most keys are launched first.
 #pragma once
 
 namespace pakv {
@@ -47,7 +51,7 @@ struct PrefillArgs {
   int32_t group;
   int32_t stride;
   int32_t max_chunk;            // host bound on every chunk's length
-  int32_t row_blocks;           // 64-row blocks per (sequence, KV head) in the grid
+  int32_t row_blocks;           // 128-row blocks per (sequence, KV head) in the grid
   float scale_log2;
 };
 
@@ -162,7 +166,7 @@ struct PrefillPair {
   u32x4 v[D / 16];        // O^T A operands: dwords 0-1 page 0, 2-3 page 1
 };
 
-template <int D>
+template <int D, int RG>
 struct PrefillWave {
   const uint16_t* ktile;  // K pool + KV head tile of page 0
   const uint16_t* vtile;
@@ -171,97 +175,94 @@ struct PrefillWave {
   int num_pages;          // pool size (page ids are clamped into it)
   int key_pages;          // pages holding positions 0 .. last_pos
   int last_pos;           // position of the wave's last token (keys past it are zeroed)
-  int pos;                // this lane's query position (rows past the chunk: last_pos)
-  uint32_t koff;          // lane's element offset inside a K tile: key r, dims 8 grp
-  uint32_t voff;          // lane's element offset inside a V tile: dim r, slots 4 grp
+  int pos[RG];            // this lane's query position per row group (rows past the chunk: last_pos)
+  uint32_t koff;          // lane's element offset inside a K tile
+  uint32_t voff;          // lane's element offset inside a V tile
+  bool k_second;          // this lane's K rows come from the pair's second page
+  bool v_second;          // this lane's V slots come from the pair's second page
   float sl2;
-  bf16x8 qf[D / 32];      // the lane's query row, B operand
+  bf16x8 qf[RG][D / 32];  // the lane's query row per row group, B operand
 };
 
-template <int D>
-__device__ __forceinline__ int clamp_pid(const PrefillWave<D>& w, int logical) {
+template <int D, int RG>
+__device__ __forceinline__ int clamp_pid(const PrefillWave<D, RG>& w, int logical) {
   const int p = w.bt_row[logical];
   return p < 0 ? 0 : (p >= w.num_pages ? w.num_pages - 1 : p);
 }
 
-template <int D>
-__device__ __forceinline__ void prefill_issue(const PrefillWave<D>& w, PrefillPair<D>& buf, int pr) {
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <int D, int RG>
+__device__ __forceinline__ void prefill_issue(const PrefillWave<D, RG>& w, PrefillPair<D>& buf, int pr) {
   constexpr int KK = D / 32;
   constexpr int MT = D / 16;
   const int pa = clamp_pid(w, 2 * pr);
   const int pb = clamp_pid(w, min(2 * pr + 1, w.key_pages - 1));   // a missing page re-reads the first
-  const uint16_t* ka = w.ktile + (size_t)pa * w.page_elems + w.koff;
-  const uint16_t* kb = w.ktile + (size_t)pb * w.page_elems + w.koff;
-  const uint16_t* va = w.vtile + (size_t)pa * w.page_elems + w.voff;
-  const uint16_t* vb = w.vtile + (size_t)pb * w.page_elems + w.voff;
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    buf.k[0][kk] = *(const u32x4*)(ka + 32 * kk);
-    buf.k[1][kk] = *(const u32x4*)(kb + 32 * kk);
-  }
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const u32x2 lo = *(const u32x2*)(va + mt * 16 * kPage);
-    const u32x2 hi = *(const u32x2*)(vb + mt * 16 * kPage);
-    buf.v[mt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-  }
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-template <int D>
-__device__ __forceinline__ void prefill_compute(const PrefillWave<D>& w, PrefillPair<D>& buf, int pr,
-                                                SoftmaxState<D>& st, int grp) {
-  constexpr int KK = D / 32;
-  constexpr int MT = D / 16;
-  f32x4 sc[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    sc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf.k[j][kk]), w.qf[kk], sc[j], 0, 0, 0);
-  }
-  // element e = 4 j + i is key position 32 pr + 16 j + 4 grp + i
-  const int key0 = 32 * pr + 4 * grp;
-  float sv[8];
-  float mx = -INFINITY;
+  const uint16_t* kp = w.ktile + (size_t)(w.k_second ? pb : pa) * w.page_elems + w.koff;
+  const uint16_t* vp = w.vtile + (size_t)(w.v_second ? pb : pa) * w.page_elems + w.voff;
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x = sc[j][i] * w.sl2;
-      x = (key0 + 16 * j + i <= w.pos) ? x : -INFINITY;
-      sv[4 * j + i] = x;
-      mx = fmaxf(mx, x);
+    for (int kk = 0; kk < KK; ++kk) buf.k[j][kk] = *(const u32x4*)(kp + 4 * j * D + 8 * kk);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) buf.v[mt] = *(const u32x4*)(vp + mt * 16 * kPage);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int D, int RG>
+__device__ __forceinline__ void prefill_compute(const PrefillWave<D, RG>& w, PrefillPair<D>& buf, int pr,
+                                                SoftmaxState<D> (&st)[RG], int grp) {
+  constexpr int KK = D / 32;
+  constexpr int MT = D / 16;
+  // element e = 4 j + i is key position 32 pr + 8 grp + 4 j + i
+  const int key0 = 32 * pr + 8 * grp;
+  bf16x8 ph[RG], pl[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    f32x4 sc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      sc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf.k[j][kk]), w.qf[g][kk], sc[j], 0, 0, 0);
     }
-  mx = xor_max(mx, 16);
-  mx = xor_max(mx, 32);
-  const float m_new = fmaxf(st.m, mx);
-  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-  float psum = 0.f;
-  bf16x8 ph, pl;
+    float sv[8];
+    float mx = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float p = __builtin_amdgcn_exp2f(sv[e] - m_new);
-    psum += p;
-    const __bf16 hi = (__bf16)p;
-    ph[e] = hi;
-    pl[e] = (__bf16)(p - (float)hi);
-  }
-  st.l = st.l * alpha + psum;
-  st.m = m_new;
-  if (__ballot(alpha != 1.f)) {
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) st.acc[mt] *= alpha;
+      for (int i = 0; i < 4; ++i) {
+        float x = sc[j][i] * w.sl2;
+        x = (key0 + 4 * j + i <= w.pos[g]) ? x : -INFINITY;
+        sv[4 * j + i] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = xor_max(mx, 16);
+    mx = xor_max(mx, 32);
+    const float m_new = fmaxf(st[g].m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(st[g].m - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = __builtin_amdgcn_exp2f(sv[e] - m_new);
+      psum += p;
+      const __bf16 hi = (__bf16)p;
+      ph[g][e] = hi;
+      pl[g][e] = (__bf16)(p - (float)hi);
+    }
+    st[g].l = st[g].l * alpha + psum;
+    st[g].m = m_new;
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) st[g].acc[mt] *= alpha;
+    }
   }
   // keys past the wave's last position may be unwritten (NaN): zero their V
-  // (dword w holds keys 2w, 2w+1 of the lane's 8: page w / 2, slots 4 grp + 2 (w % 2))
+  // (dword q holds the lane's keys 2q, 2q+1: positions key0 + 2q, key0 + 2q + 1)
   if (32 * pr + 32 > w.last_pos + 1) {
     uint32_t keep[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int k0 = key0 + 16 * (q >> 1) + 2 * (q & 1);
+      const int k0 = key0 + 2 * q;
       keep[q] = (k0 <= w.last_pos ? 0x0000FFFFu : 0u) | (k0 + 1 <= w.last_pos ? 0xFFFF0000u : 0u);
     }
 #pragma unroll
@@ -270,18 +271,20 @@ __device__ __forceinline__ void prefill_compute(const PrefillWave<D>& w, Prefill
       for (int q = 0; q < 4; ++q) buf.v[mt][q] &= keep[q];
   }
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    st.acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf.v[mt]), ph, st.acc[mt], 0, 0, 0);
-    st.acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf.v[mt]), pl, st.acc[mt], 0, 0, 0);
-  }
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      st[g].acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf.v[mt]), ph[g], st[g].acc[mt], 0, 0, 0);
+      st[g].acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf.v[mt]), pl[g], st[g].acc[mt], 0, 0, 0);
+    }
   __builtin_amdgcn_sched_barrier(0);
 }
 
 // All pairs 0 .. npairs-1 of one wave, the next pair's loads in flight while
 // the current one computes (two register buffers, exact peeled loop).
-template <int D>
-__device__ __forceinline__ void prefill_stream(const PrefillWave<D>& w, int npairs, SoftmaxState<D>& st,
-                                               int grp) {
+template <int D, int RG>
+__device__ __forceinline__ void prefill_stream(const PrefillWave<D, RG>& w, int npairs,
+                                               SoftmaxState<D> (&st)[RG], int grp) {
   const int n = __builtin_amdgcn_readfirstlane(npairs);
   if (n <= 0) return;
   PrefillPair<D> b0, b1;
@@ -302,12 +305,25 @@ __device__ __forceinline__ void prefill_stream(const PrefillWave<D>& w, int npai
   }
 }
 
-// Grid: (KV head fastest, then sequence, then row block from the last one
-// down, so the blocks that see the most keys start first).
+// Two groups of 16 rows per wave: every K/V operand loaded feeds both.
 template <int D>
-__global__ __launch_bounds__(256, occupancy(D)) void prefill_kernel(PrefillArgs a) {
+__host__ __device__ constexpr int prefill_row_groups() { return 2; }
+// Waves per SIMD the register budget allows (185 / 320 registers per lane).
+template <int D>
+__host__ __device__ constexpr int prefill_occupancy() { return D == 64 ? 2 : 1; }
+// rows per workgroup: 4 waves x 16 rows x row groups
+template <int D>
+__host__ __device__ constexpr int prefill_block_rows() { return 64 * prefill_row_groups<D>(); }
+
+// Grid: (KV head fastest, then sequence, then row block from the last one
+// down, so the blocks that see the most keys start first). Wave w of a
+// block takes rows w * 16 * RG .. + 16 * RG - 1, in RG groups of 16.
+template <int D>
+__global__ __launch_bounds__(256, prefill_occupancy<D>()) void prefill_kernel(PrefillArgs a) {
   constexpr int KK = D / 32;
   constexpr int MT = D / 16;
+  constexpr int RG = prefill_row_groups<D>();
+  constexpr int WROWS = 16 * RG;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15;
@@ -319,41 +335,57 @@ __global__ __launch_bounds__(256, occupancy(D)) void prefill_kernel(PrefillArgs 
   const int G = a.group;
   const Chunk ch = load_chunk(a.query_start, a.ctx_before, b, a.num_rows, a.max_chunk, a.stride);
   const int rows = ch.n * G;
-  const int rho0 = rb * 64 + wave * 16;        // the wave's first row
+  const int rho0 = rb * (4 * WROWS) + wave * WROWS;   // the wave's first row
   if (rho0 >= rows) return;
-  const int rho_last = min(rho0 + 15, rows - 1);
-  const int rho = rho0 + r;
-  const bool valid = rho < rows;
-  const int t = (valid ? rho : rho_last) / G;  // chunk token of this lane's row
-  const int h = (valid ? rho : rho_last) - t * G;
+  const int rho_last = min(rho0 + WROWS - 1, rows - 1);
 
-  PrefillWave<D> w;
+  PrefillWave<D, RG> w;
   w.last_pos = ch.c + rho_last / G;
-  w.pos = ch.c + t;
   w.key_pages = (w.last_pos + kPage) / kPage;
   w.num_pages = a.num_pages;
   w.bt_row = a.block_tables + (size_t)b * a.stride;
   w.page_elems = (size_t)a.num_kv_heads * kPage * D;
   w.ktile = a.kpool + (size_t)kvh * kPage * D;
   w.vtile = a.vpool + (size_t)kvh * kPage * D;
-  w.koff = (uint32_t)(r * D + 8 * grp);
-  w.voff = (uint32_t)(r * kPage + 4 * grp);
+  // pair-mixed rows: QK row r of MFMA j is page r / 8, slot 8 ((r / 4) % 2) + 4 j + r % 4,
+  // so lane group grp ends up with slots 8 (grp % 2) + 0..7 of page grp / 2 for PV
+  w.koff = (uint32_t)((8 * ((r >> 2) & 1) + (r & 3)) * D + (D / 4) * grp);
+  w.voff = (uint32_t)(r * kPage + 8 * (grp & 1));
+  w.k_second = (r >> 3) != 0;
+  w.v_second = (grp >> 1) != 0;
+  const int qdim0 = (D / 4) * grp, qdim_step = 8;
   w.sl2 = a.scale_log2;
-  const size_t qrow = ((size_t)(ch.r0 + t) * a.num_q_heads + (size_t)kvh * G + h) * D;
+  size_t qrow[RG];
+  bool valid[RG];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk)
-    w.qf[kk] = as_bf16x8(valid ? *(const u32x4*)(a.q + qrow + 32 * kk + 8 * grp) : u32x4{0u, 0u, 0u, 0u});
+  for (int g = 0; g < RG; ++g) {
+    const int rho = rho0 + 16 * g + r;
+    valid[g] = rho < rows;
+    const int t = (valid[g] ? rho : rho_last) / G;    // chunk token of this lane's row
+    const int h = (valid[g] ? rho : rho_last) - t * G;
+    w.pos[g] = ch.c + t;
+    qrow[g] = ((size_t)(ch.r0 + t) * a.num_q_heads + (size_t)kvh * G + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      w.qf[g][kk] = as_bf16x8(valid[g] ? *(const u32x4*)(a.q + qrow[g] + qdim0 + qdim_step * kk)
+                                       : u32x4{0u, 0u, 0u, 0u});
+  }
 
-  SoftmaxState<D> st;
-  init_state(st);
-  prefill_stream(w, (w.key_pages + 1) >> 1, st, grp);
-  st.l += __shfl_xor(st.l, 16, 64);
-  st.l += __shfl_xor(st.l, 32, 64);
-  if (valid) {
-    const float inv = 1.f / st.l;
-    float* o = a.out + qrow + 4 * grp;
+  SoftmaxState<D> st[RG];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) *(f32x4*)(o + 16 * mt) = st.acc[mt] * inv;
+  for (int g = 0; g < RG; ++g) init_state(st[g]);
+  prefill_stream(w, (w.key_pages + 1) >> 1, st, grp);
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    float l = st[g].l;
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (valid[g]) {
+      const float inv = 1.f / l;
+      float* o = a.out + qrow[g] + 4 * grp;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) *(f32x4*)(o + 16 * mt) = st[g].acc[mt] * inv;
+    }
   }
 }
 

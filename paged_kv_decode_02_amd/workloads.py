@@ -350,6 +350,121 @@ def make_workload(name: str) -> Workload:
 WORKLOADS = ["tiny", "c2", "c3", "c4", "c5"]
 
 
+# ------------------------------------------------------------------ prefill
+@dataclass
+class PrefillWorkload:
+    """A chunk of new tokens per sequence on top of ``ctx_before`` cached ones.
+
+    ``base`` carries the pool and block tables; its ``ctx_lens`` are the
+    lengths after the chunk, and only the ``ctx_before`` tokens are valid in
+    the pool (the chunk's slots are NaN until the chunk is written). Row
+    arrays are layer-major: q ``[L][N][Hq][d]``, k/v ``[L][N][Hkv][d]``, with
+    sequence ``b`` owning rows ``query_start[b] ..``.
+    """
+    base: Workload
+    ctx_before: np.ndarray   # int32 [B]
+    chunks: np.ndarray       # int32 [B]
+
+    @property
+    def name(self) -> str:
+        return self.base.name
+
+    @property
+    def query_start(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.chunks)]).astype(np.int32)
+
+    @property
+    def num_rows(self) -> int:
+        return int(self.chunks.sum())
+
+    def _heads(self, which: str) -> int:
+        return self.base.num_q_heads if which == "q" else self.base.num_kv_heads
+
+    def _stream(self, which: str) -> int:
+        return {"q": STREAM_Q, "k": STREAM_K_NEW, "v": STREAM_V_NEW}[which]
+
+    def rows_bits(self, which: str, layer: int, rows) -> np.ndarray:
+        """Host copy of the listed rows of one layer: ``[len(rows)][H][d]``."""
+        w = self.base
+        per_row = self._heads(which) * w.head_dim
+        rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+        idx = (layer * self.num_rows + rows)[:, None] * per_row + np.arange(per_row, dtype=np.int64)[None, :]
+        v = values_np(w.seed, self._stream(which), idx, w.table())
+        return v.reshape(rows.size, self._heads(which), w.head_dim)
+
+    def rows_device(self, which: str, device):
+        """All layers' rows made on ``device``, bit-identical to ``rows_bits``
+        (int16 ``[L][N][H][d]``)."""
+        import torch
+        w = self.base
+        shape = (w.num_layers, self.num_rows, self._heads(which), w.head_dim)
+        total = int(np.prod(shape))
+        table = torch.from_numpy(w.table().view(np.int16)).to(device)
+        out = torch.empty(total, dtype=torch.int16, device=device)
+        for start in range(0, total, 1 << 26):
+            end = min(total, start + (1 << 26))
+            idx = torch.arange(start, end, dtype=torch.int64, device=device)
+            out[start:end] = table[hash32(w.seed, self._stream(which), idx) >> 16]
+            del idx
+        return out.view(shape)
+
+    def attended_pairs(self) -> int:
+        """(query token, key) pairs of one layer and one query head: token i of
+        sequence b sees ctx_before[b] + i + 1 keys."""
+        c = self.ctx_before.astype(np.int64)
+        n = self.chunks.astype(np.int64)
+        return int((n * c + n * (n + 1) // 2).sum())
+
+    def flops_per_layer(self) -> int:
+        """2 d flops for the score and 2 d for the weighted value, per query
+        head and attended pair."""
+        w = self.base
+        return 4 * w.head_dim * w.num_q_heads * self.attended_pairs()
+
+    def write_bytes_per_layer(self) -> int:
+        w = self.base
+        return self.num_rows * w.num_kv_heads * w.head_dim * 2 * 2
+
+
+def make_prefill_workload(name: str) -> PrefillWorkload:
+    """Prefill configurations: ``prefill`` is the 16-layer prefill of 8 prompts
+    of 2048 tokens (the context limit of the samir-vllm engine) at the
+    Llama-3.2-1B attention shape; ``prefill_d128`` is 4 prompts of 4096 tokens
+    at the 28q/4kv, d=128 shape, one layer; ``prefill_chunked`` continues 8
+    caches of U[0, 4096] tokens with 512-token chunks (one layer, d=64)."""
+    if name == "prefill":
+        seed, layers, hq, hkv, d = 1006, 16, 32, 8, 64
+        before = np.zeros(8, np.int32)
+        chunks = np.full(8, 2048, np.int32)
+        stride = 128
+    elif name == "prefill_d128":
+        seed, layers, hq, hkv, d = 1007, 1, 28, 4, 128
+        before = np.zeros(4, np.int32)
+        chunks = np.full(4, 4096, np.int32)
+        stride = 256
+    elif name == "prefill_chunked":
+        seed, layers, hq, hkv, d = 1008, 1, 32, 8, 64
+        rng0 = np.random.default_rng(seed)
+        before = rng0.integers(0, 4097, 8).astype(np.int32)
+        chunks = np.full(8, 512, np.int32)
+        stride = 288
+    else:
+        raise ValueError(f"unknown prefill workload {name!r}")
+    rng = np.random.default_rng(seed + 100)
+    total = before + chunks
+    need = np.broadcast_to(_pages(total), (layers, total.size)).copy()
+    demand = int(need.sum())
+    num_pages = demand + -(-demand // 100) + 1
+    bt = _deal_pages(rng, need, num_pages, stride, interleave=True)
+    base = _finish(name, seed, layers, hq, hkv, d, 1.0, total, bt, num_pages, False,
+                   f"demand {demand} pages + 1% slack, interleaved; chunk slots NaN until written")
+    base.page_valid = _page_valid(bt, before, num_pages)
+    return PrefillWorkload(base=base, ctx_before=before, chunks=chunks)
+
+
+PREFILL_WORKLOADS = ["prefill", "prefill_d128", "prefill_chunked"]
+
+
 def custom(seed: int, ctx_lens: List[int], num_q_heads: int = 32, num_kv_heads: int = 8,
            head_dim: int = 64, num_layers: int = 1, sigma: float = 1.0,
            append: bool = False, stride: Optional[int] = None, extra_pages: int = 3,
