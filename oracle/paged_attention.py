@@ -27,7 +27,7 @@ Sources (web pages, cited by title and section):
   contiguous grouping, q head i uses KV head i / (q heads per KV head), and a
   token-major contiguous KV cache ([token][kv_head][head_dim]).
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
 
 * The attention is the standard scaled dot-product softmax attention
   (the pages name self-attention but never print the formula); the scale is an

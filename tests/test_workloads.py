@@ -99,3 +99,40 @@ def test_shapes_follow_printed_architecture():
     w = W.make_workload("c3")
     assert w.num_kv_heads * 16 * w.head_dim * 2 * 2 == 32 << 10
     assert (geo["default_pool_mib"] << 20) // (32 << 10) == 4096
+
+
+@pytest.mark.parametrize("name", W.PREFILL_WORKLOADS)
+def test_prefill_workloads(name):
+    import torch
+    w = W.make_prefill_workload(name)
+    again = W.make_prefill_workload(name)
+    assert np.array_equal(w.ctx_before, again.ctx_before) and np.array_equal(w.chunks, again.chunks)
+    assert np.array_equal(w.base.block_tables, again.base.block_tables)
+    qs = w.query_start
+    assert qs[0] == 0 and qs[-1] == w.num_rows and np.all(np.diff(qs) == w.chunks)
+    total = w.ctx_before + w.chunks
+    assert np.array_equal(w.base.ctx_lens, total)
+    assert int(total.max()) <= w.base.stride * W.PAGE
+    used = np.concatenate([w.base.sequence_pages(l, b) for l in range(w.base.num_layers)
+                           for b in range(len(total))])
+    assert np.unique(used).size == used.size and used.min() >= 0 and used.max() < w.base.num_pages
+    assert int(w.base.page_valid.sum()) == int(w.ctx_before.sum()) * w.base.num_layers
+    # only the cached tokens are valid in the pool; the chunk's slots are poison
+    b = int(np.argmax(w.ctx_before)) if w.ctx_before.max() > 0 else 0
+    c = int(w.ctx_before[b])
+    page = int(w.base.block_tables[0, b, c // W.PAGE])
+    kp = w.base.pool_pages_bits("k", [page])[0]
+    slots = np.arange(W.PAGE)
+    assert np.all((kp[:, slots >= c % W.PAGE] == W.NAN_BITS))
+    assert not np.any(kp[:, slots < c % W.PAGE] == W.NAN_BITS)
+    # row generators: host rows equal the device-path rows, layers differ
+    rows = np.array([0, 1, w.num_rows - 1])
+    small = W.PrefillWorkload(base=w.base, ctx_before=w.ctx_before, chunks=w.chunks)
+    dev = small.rows_device("k", "cpu") if w.base.num_layers * w.num_rows * w.base.num_kv_heads * w.base.head_dim < (1 << 26) else None
+    host0 = w.rows_bits("k", 0, rows)
+    if dev is not None:
+        assert np.array_equal(dev[0, rows].numpy().view(np.uint16), host0)
+    if w.base.num_layers > 1:
+        assert not np.array_equal(w.rows_bits("k", 1, rows), host0)
+    assert w.flops_per_layer() == 4 * w.base.head_dim * w.base.num_q_heads * sum(
+        int(n) * int(cb) + int(n) * (int(n) + 1) // 2 for n, cb in zip(w.chunks, w.ctx_before))
