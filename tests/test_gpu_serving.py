@@ -92,3 +92,76 @@ def test_serving_loop_over_scheduler_pages():
     assert np.array_equal(k_dev.cpu().numpy().view(np.uint16), k_host)
     assert np.array_equal(v_dev.cpu().numpy().view(np.uint16), v_host)
     log(f"serving loop: {steps} steps, {checked} decode launches checked against the oracle")
+
+
+def test_chunked_prefill_then_decode_over_scheduler_pages():
+    """Requests from the scheduler are prefilled in chunks with pa_prefill (a
+    shared-prefix request continues from its parent's cached pages), then
+    decode one token per step. Every prefill row and decode output is checked
+    against the oracle over a host mirror of the pool."""
+    import torch
+    dev = device()
+    P, L, MB, STRIDE = 80, 2, 4, 24
+    HQ, HKV, D = 28, 4, 128
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    rng = np.random.default_rng(77)
+    sched = B.Scheduler(P, L, MB, STRIDE)
+    k_host = np.full((P, HKV, 16, D), NAN, np.uint16)
+    v_host = np.full((P, HKV, D, 16), NAN, np.uint16)
+    k_dev = torch.from_numpy(k_host.view(np.int16).copy()).to(dev)
+    v_dev = torch.from_numpy(v_host.view(np.int16).copy()).to(dev)
+    pool = B.Pool(k_dev, v_dev)
+    t = lambda a, dt=np.int32: torch.from_numpy(np.ascontiguousarray(a).astype(dt)).to(dev)
+    bits = lambda shape: f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+
+    a = sched.submit(150, 3)
+    b = sched.submit(37, 4)
+    assert sched.admit() == [a, b]
+    prompt = {a: 150, b: 37}
+    budget = {a: 153, b: 41}
+    CHUNK = 64
+    child = None
+    checked = 0
+    for step in range(40):
+        if not budget:
+            break
+        ctx0 = sched.context_lens.copy()
+        bt_all = sched.block_tables.copy()
+        # every running request takes its next chunk: up to CHUNK prompt tokens, or one decode token
+        lens = np.zeros(MB, np.int64)
+        owner = {}
+        for rid in list(budget):
+            slot = sched.slot(rid)
+            if slot < 0:
+                continue
+            owner[slot] = rid
+            c = int(ctx0[slot])
+            lens[slot] = min(CHUNK, prompt[rid] - c) if c < prompt[rid] else 1
+        qs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        n = int(qs[-1])
+        q, kr, vr = bits((n, HQ, D)), bits((n, HKV, D)), bits((n, HKV, D))
+        for layer in range(L):
+            bt = np.where(bt_all[layer] < 0, 0, bt_all[layer]).astype(np.int32)
+            out = B.prefill(pool, t(q.view(np.int16), np.int16), t(kr.view(np.int16), np.int16),
+                            t(vr.view(np.int16), np.int16), t(qs), t(bt), t(ctx0), scale,
+                            int(lens.max())).cpu().numpy()
+            ref, k_host, v_host = oracle.prefill_attention(q, k_host, v_host, kr, vr, qs, bt, ctx0, scale)
+            check_parity(out, ref, f"step {step} layer {layer}")
+            checked += 1
+        for slot, rid in owner.items():
+            sched.advance(rid, int(lens[slot]))
+        if child is None and sched.context_lens[sched.slot(a)] >= 150:
+            child = sched.submit_shared(a, 150, 170, 2)          # 9 full pages per layer shared
+            prompt[child], budget[child] = 170, 172
+            assert sched.admit() == [child]
+            assert sched.context_lens[sched.slot(child)] == 144
+        for rid in list(budget):
+            slot = sched.slot(rid)
+            if slot >= 0 and sched.context_lens[slot] >= budget[rid]:
+                sched.finish(rid)
+                del budget[rid]
+    assert not budget and child is not None
+    assert np.array_equal(k_dev.cpu().numpy().view(np.uint16), k_host)
+    assert np.array_equal(v_dev.cpu().numpy().view(np.uint16), v_host)
+    assert sched.stats() == {"free_pages": P, "queued": 0, "running": 0}
+    log(f"chunked prefill loop: {checked} prefill launches checked")
