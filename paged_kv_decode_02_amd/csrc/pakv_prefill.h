@@ -175,6 +175,7 @@ struct PrefillWave {
   int num_pages;          // pool size (page ids are clamped into it)
   int key_pages;          // pages holding positions 0 .. last_pos
   int last_pos;           // position of the wave's last token (keys past it are zeroed)
+  int first_pos;          // position of the wave's first token (keys up to it are seen by every row)
   int pos[RG];            // this lane's query position per row group (rows past the chunk: last_pos)
   uint32_t koff;          // lane's element offset inside a K tile
   uint32_t voff;          // lane's element offset inside a V tile
@@ -207,13 +208,22 @@ __device__ __forceinline__ void prefill_issue(const PrefillWave<D, RG>& w, Prefi
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// How far (log2 units) a row's running max may trail its true max before the
+// accumulators are rescaled: weights then stay below 2^8, and a rescale
+// happens only when a row's maximum grows by more than that.
+constexpr float kLazyMax = 8.f;
+
 template <int D, int RG>
 __device__ __forceinline__ void prefill_compute(const PrefillWave<D, RG>& w, PrefillPair<D>& buf, int pr,
                                                 SoftmaxState<D> (&st)[RG], int grp) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
   constexpr int KK = D / 32;
   constexpr int MT = D / 16;
-  // element e = 4 j + i is key position 32 pr + 8 grp + 4 j + i
+  // element e = 4 j + i is key position key0 + e
   const int key0 = 32 * pr + 8 * grp;
+  // only a pair that some row of the wave cannot see whole needs the mask
+  const bool diag = 32 * pr + 31 > w.first_pos;
   bf16x8 ph[RG], pl[RG];
 #pragma unroll
   for (int g = 0; g < RG; ++g) {
@@ -226,35 +236,40 @@ __device__ __forceinline__ void prefill_compute(const PrefillWave<D, RG>& w, Pre
         sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf.k[j][kk]), w.qf[g][kk], sc[j], 0, 0, 0);
     }
     float sv[8];
-    float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int e = 0; e < 8; ++e) sv[e] = sc[e >> 2][e & 3];
+    if (diag) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = sc[j][i] * w.sl2;
-        x = (key0 + 4 * j + i <= w.pos[g]) ? x : -INFINITY;
-        sv[4 * j + i] = x;
-        mx = fmaxf(mx, x);
-      }
+      for (int e = 0; e < 8; ++e) sv[e] = (key0 + e <= w.pos[g]) ? sv[e] : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     mx = xor_max(mx, 16);
     mx = xor_max(mx, 32);
-    const float m_new = fmaxf(st[g].m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(st[g].m - m_new);
+    // raw scores times a positive sl2 (the sign of the scale is folded into q)
+    const float mx2 = mx * w.sl2;
+    const float m_old = st[g].m;
+    const float m_new = mx2 > m_old + kLazyMax ? mx2 : m_old;
+    const float alpha = __builtin_amdgcn_exp2f(m_old - m_new);
     float psum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = __builtin_amdgcn_exp2f(sv[e] - m_new);
-      psum += p;
-      const __bf16 hi = (__bf16)p;
-      ph[g][e] = hi;
-      pl[g][e] = (__bf16)(p - (float)hi);
+    for (int e = 0; e < 8; e += 2) {
+      const f32x2 pv = {__builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], w.sl2, -m_new)),
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e + 1], w.sl2, -m_new))};
+      psum += pv[0] + pv[1];
+      const bf16x2 hi = __builtin_convertvector(pv, bf16x2);
+      const bf16x2 lo = __builtin_convertvector(pv - __builtin_convertvector(hi, f32x2), bf16x2);
+      ph[g][e] = hi[0];
+      ph[g][e + 1] = hi[1];
+      pl[g][e] = lo[0];
+      pl[g][e + 1] = lo[1];
     }
     st[g].l = st[g].l * alpha + psum;
-    st[g].m = m_new;
-    if (__ballot(alpha != 1.f)) {
+    if (__ballot(m_new != m_old)) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) st[g].acc[mt] *= alpha;
     }
+    st[g].m = m_new;
   }
   // keys past the wave's last position may be unwritten (NaN): zero their V
   // (dword q holds the lane's keys 2q, 2q+1: positions key0 + 2q, key0 + 2q + 1)
@@ -341,6 +356,7 @@ __global__ __launch_bounds__(256, prefill_occupancy<D>()) void prefill_kernel(Pr
 
   PrefillWave<D, RG> w;
   w.last_pos = ch.c + rho_last / G;
+  w.first_pos = ch.c + rho0 / G;
   w.key_pages = (w.last_pos + kPage) / kPage;
   w.num_pages = a.num_pages;
   w.bt_row = a.block_tables + (size_t)b * a.stride;
@@ -354,7 +370,11 @@ __global__ __launch_bounds__(256, prefill_occupancy<D>()) void prefill_kernel(Pr
   w.k_second = (r >> 3) != 0;
   w.v_second = (grp >> 1) != 0;
   const int qdim0 = (D / 4) * grp, qdim_step = 8;
-  w.sl2 = a.scale_log2;
+  // the softmax needs sl2 > 0: a negative scale is moved into the query
+  // (exact sign flips), and a zero scale is the same as a zero query
+  const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+  const bool qzero = a.scale_log2 == 0.f;
+  w.sl2 = qzero ? 1.f : fabsf(a.scale_log2);
   size_t qrow[RG];
   bool valid[RG];
 #pragma unroll
@@ -367,8 +387,8 @@ __global__ __launch_bounds__(256, prefill_occupancy<D>()) void prefill_kernel(Pr
     qrow[g] = ((size_t)(ch.r0 + t) * a.num_q_heads + (size_t)kvh * G + h) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      w.qf[g][kk] = as_bf16x8(valid[g] ? *(const u32x4*)(a.q + qrow[g] + qdim0 + qdim_step * kk)
-                                       : u32x4{0u, 0u, 0u, 0u});
+      w.qf[g][kk] = as_bf16x8((valid[g] && !qzero) ? *(const u32x4*)(a.q + qrow[g] + qdim0 + qdim_step * kk) ^ qflip
+                                                    : u32x4{0u, 0u, 0u, 0u});
   }
 
   SoftmaxState<D> st[RG];

@@ -16,13 +16,13 @@ pytestmark = pytest.mark.gpu
 
 
 class PrefillCase:
-    def __init__(self, seed, hq, hkv, d, befores, chunks, sigma=1.0):
+    def __init__(self, seed, hq, hkv, d, befores, chunks, sigma=1.0, scale=None):
         import torch
         dev = device()
         rng = np.random.default_rng(seed)
         (self.q, self.kc, self.vc, self.k_pool, self.v_pool, self.bt, self.qs, self.bef,
          self.k_rows, self.v_rows) = make_prefill_case(rng, hq, hkv, d, befores, chunks, sigma=sigma)
-        self.scale = np.float32(1.0 / np.sqrt(d))
+        self.scale = np.float32(1.0 / np.sqrt(d)) if scale is None else np.float32(scale)
         t = lambda a, dt=np.int16: torch.from_numpy(np.ascontiguousarray(a).view(dt) if dt == np.int16
                                                      else np.ascontiguousarray(a.astype(dt))).to(dev)
         self.k_dev, self.v_dev = t(self.k_pool), t(self.v_pool)
@@ -122,3 +122,15 @@ def test_long_prompt_sampled_rows(d, hq, hkv):
             ref = np.stack([oracle.attend_one_head(qr[h], kc[:p + 1, h // g], vc[:p + 1, h // g], float(c.scale))
                             for h in range(hq)])
             check_parity(out[row], ref, f"long prefill b={b} row {i}")
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 3.0])
+def test_prefill_any_scale(scale):
+    """Negative, zero and large softmax scales (a negative scale reverses the
+    order of the scores; zero gives the mean of the visible values)."""
+    c = PrefillCase(12, 32, 8, 64, [0, 21], [70, 45], scale=scale)
+    log(f"prefill scale {scale}: chunks=[70,45] before=[0,21] entry=pa_prefill")
+    out = c.run().cpu().numpy()
+    ref, _, _ = oracle.prefill_attention(c.q, c.k_pool, c.v_pool, c.k_rows, c.v_rows, c.qs, c.bt, c.bef,
+                                         c.scale)
+    check_parity(out, ref, f"prefill scale {scale}")
