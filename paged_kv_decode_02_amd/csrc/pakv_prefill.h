@@ -14,9 +14,11 @@
 // Attention work decomposition. For one (sequence, KV head) the chunk's
 // query rows are the (token, head) pairs of the G query heads of that KV
 // head, row index rho = token * G + head. A workgroup of 4 wavefronts takes
-// 128 consecutive rows, 32 per wave in two groups of 16; each wave streams
-// the key pages its rows can see (up to the position of its last token), two
-// pages per step, and every K/V operand it loads feeds both row groups:
+// 128 consecutive rows, 32 per wave in two groups of 16, and streams the key
+// pages its rows can see (up to the position of its last token), two pages
+// per step. The workgroup loads each page pair's K and V once into LDS,
+// stored in matrix-core operand order; every wave reads its operands from
+// there and feeds both of its row groups with them:
 //
 //   S^T = K Q^T on the matrix cores (v_mfma_f32_16x16x32_bf16): A = 16 keys
 //     x 32 head dims, B = 32 head dims x one group's 16 rows. The 16 A rows
@@ -24,13 +26,13 @@
 //     8 ((r / 4) % 2) + 4 j + r % 4), so that lane (r = lane % 16,
 //     grp = lane / 16) ends up with slots 8 (grp % 2) + 0..7 of page grp / 2
 //     for row r: 8 consecutive keys, positions 32 pair + 8 grp + 0..7;
-//   causal mask by select, FP32 online softmax per row (the 4 lanes holding a
-//     row reduce their maxima with two xor shuffles);
+//   causal mask by select (only on pairs that cross the diagonal), FP32
+//     online softmax per row (the 4 lanes holding a row reduce their maxima
+//     with two xor shuffles), the running max allowed to trail by 2^8;
 //   O^T += V^T P^T on the matrix cores: A = V^T (16 head dims x those 8 keys
-//     per lane group: one 16-byte load from the slot-minor V row), B = P^T,
+//     per lane group: 16 contiguous bytes of a slot-minor V row), B = P^T,
 //     P split into BF16 hi + lo as in decode.
-// The waves share nothing; there is no LDS and no barrier. The row blocks
-// that see the most keys are launched first.
+// The row blocks that see the most keys are launched first.
 #pragma once
 
 namespace pakv {
@@ -162,8 +164,8 @@ __global__ __launch_bounds__(256) void kv_write_kernel(WriteArgs a) {
 // -------------------------------------------------------------- attention
 template <int D>
 struct PrefillPair {
-  u32x4 k[2][D / 32];     // S^T A operands: page j of the pair, k-step kk
-  u32x4 v[D / 16];        // O^T A operands: dwords 0-1 page 0, 2-3 page 1
+  u32x4 k[2][D / 32];     // S^T A operands: MFMA j of the pair, k-step kk
+  u32x4 v[D / 16];        // O^T A operands: head-dim tile mt
 };
 
 template <int D, int RG>
@@ -173,14 +175,10 @@ struct PrefillWave {
   const int32_t* bt_row;  // the sequence's block-table row
   size_t page_elems;
   int num_pages;          // pool size (page ids are clamped into it)
-  int key_pages;          // pages holding positions 0 .. last_pos
+  int key_pages;          // pages the workgroup reads (positions 0 .. its last token)
   int last_pos;           // position of the wave's last token (keys past it are zeroed)
   int first_pos;          // position of the wave's first token (keys up to it are seen by every row)
   int pos[RG];            // this lane's query position per row group (rows past the chunk: last_pos)
-  uint32_t koff;          // lane's element offset inside a K tile
-  uint32_t voff;          // lane's element offset inside a V tile
-  bool k_second;          // this lane's K rows come from the pair's second page
-  bool v_second;          // this lane's V slots come from the pair's second page
   float sl2;
   bf16x8 qf[RG][D / 32];  // the lane's query row per row group, B operand
 };
@@ -189,23 +187,6 @@ template <int D, int RG>
 __device__ __forceinline__ int clamp_pid(const PrefillWave<D, RG>& w, int logical) {
   const int p = w.bt_row[logical];
   return p < 0 ? 0 : (p >= w.num_pages ? w.num_pages - 1 : p);
-}
-
-template <int D, int RG>
-__device__ __forceinline__ void prefill_issue(const PrefillWave<D, RG>& w, PrefillPair<D>& buf, int pr) {
-  constexpr int KK = D / 32;
-  constexpr int MT = D / 16;
-  const int pa = clamp_pid(w, 2 * pr);
-  const int pb = clamp_pid(w, min(2 * pr + 1, w.key_pages - 1));   // a missing page re-reads the first
-  const uint16_t* kp = w.ktile + (size_t)(w.k_second ? pb : pa) * w.page_elems + w.koff;
-  const uint16_t* vp = w.vtile + (size_t)(w.v_second ? pb : pa) * w.page_elems + w.voff;
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) buf.k[j][kk] = *(const u32x4*)(kp + 4 * j * D + 8 * kk);
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) buf.v[mt] = *(const u32x4*)(vp + mt * 16 * kPage);
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 // How far (log2 units) a row's running max may trail its true max before the
@@ -295,31 +276,6 @@ __device__ __forceinline__ void prefill_compute(const PrefillWave<D, RG>& w, Pre
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// All pairs 0 .. npairs-1 of one wave, the next pair's loads in flight while
-// the current one computes (two register buffers, exact peeled loop).
-template <int D, int RG>
-__device__ __forceinline__ void prefill_stream(const PrefillWave<D, RG>& w, int npairs,
-                                               SoftmaxState<D> (&st)[RG], int grp) {
-  const int n = __builtin_amdgcn_readfirstlane(npairs);
-  if (n <= 0) return;
-  PrefillPair<D> b0, b1;
-  prefill_issue(w, b0, 0);
-  int it = 0;
-  for (; it + 2 < n; it += 2) {
-    prefill_issue(w, b1, it + 1);
-    prefill_compute(w, b0, it, st, grp);
-    prefill_issue(w, b0, it + 2);
-    prefill_compute(w, b1, it + 1, st, grp);
-  }
-  if (it + 1 < n) {
-    prefill_issue(w, b1, it + 1);
-    prefill_compute(w, b0, it, st, grp);
-    prefill_compute(w, b1, it + 1, st, grp);
-  } else {
-    prefill_compute(w, b0, it, st, grp);
-  }
-}
-
 // Two groups of 16 rows per wave: every K/V operand loaded feeds both.
 template <int D>
 __host__ __device__ constexpr int prefill_row_groups() { return 2; }
@@ -330,17 +286,37 @@ __host__ __device__ constexpr int prefill_occupancy() { return D == 64 ? 2 : 1; 
 template <int D>
 __host__ __device__ constexpr int prefill_block_rows() { return 64 * prefill_row_groups<D>(); }
 
-// Grid: (KV head fastest, then sequence, then row block from the last one
-// down, so the blocks that see the most keys start first). Wave w of a
-// block takes rows w * 16 * RG .. + 16 * RG - 1, in RG groups of 16.
+// Grid: KV head fastest, then sequence, then row block from the last one
+// down, so the blocks that see the most keys start first. Wave w of a block
+// takes rows w * 32 .. w * 32 + 31 in two groups of 16. The 4 waves share
+// every K/V tile: per page pair the workgroup loads K and V once (coalesced 16-byte
+// loads, each thread its share), stores them to LDS in matrix-core operand
+// order (chunk (MFMA j, k-step kk or dim tile mt, lane) at a lane-linear
+// address, so the waves' 16-byte LDS reads are conflict-free), and every
+// wave reads its operands from there. Two LDS buffers: the next pair's
+// global loads are in flight while the current pair computes; one barrier
+// per pair.
+template <int D>
+struct PrefillLds {
+  static constexpr int kKBytes = 2 * kPage * D * 2;     // K of a pair (two pages)
+  static constexpr int kPairBytes = 2 * kKBytes;        // K and V
+  static constexpr int kPerThread = (4 * D) / 256;      // 16-byte K (and V) chunks per thread
+};
+
 template <int D>
 __global__ __launch_bounds__(256, prefill_occupancy<D>()) void prefill_kernel(PrefillArgs a) {
   constexpr int KK = D / 32;
   constexpr int MT = D / 16;
   constexpr int RG = prefill_row_groups<D>();
   constexpr int WROWS = 16 * RG;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr int BROWS = 4 * WROWS;
+  constexpr int NPT = PrefillLds<D>::kPerThread;
+  constexpr int KB = PrefillLds<D>::kKBytes;
+  constexpr int PB = PrefillLds<D>::kPairBytes;
+  __shared__ __attribute__((aligned(16))) char lds[2 * PB];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15;
   const int grp = lane >> 4;
   const int kvh = blockIdx.x % a.num_kv_heads;
@@ -350,28 +326,23 @@ __global__ __launch_bounds__(256, prefill_occupancy<D>()) void prefill_kernel(Pr
   const int G = a.group;
   const Chunk ch = load_chunk(a.query_start, a.ctx_before, b, a.num_rows, a.max_chunk, a.stride);
   const int rows = ch.n * G;
-  const int rho0 = rb * (4 * WROWS) + wave * WROWS;   // the wave's first row
-  if (rho0 >= rows) return;
-  const int rho_last = min(rho0 + WROWS - 1, rows - 1);
+  if (rb * BROWS >= rows) return;                      // the whole block is past the chunk
+  const int blk_last_pos = ch.c + min(rb * BROWS + BROWS - 1, rows - 1) / G;
+  const int blk_pages = (blk_last_pos + kPage) / kPage;
+  const int npairs = (blk_pages + 1) >> 1;
+  const int rho0 = rb * BROWS + wave * WROWS;          // the wave's first row
+  const bool active = rho0 < rows;                     // a wave past the chunk only loads
+  const int rho_last = active ? min(rho0 + WROWS - 1, rows - 1) : rows - 1;
 
   PrefillWave<D, RG> w;
   w.last_pos = ch.c + rho_last / G;
-  w.first_pos = ch.c + rho0 / G;
-  w.key_pages = (w.last_pos + kPage) / kPage;
+  w.first_pos = ch.c + min(rho0, rows - 1) / G;
+  w.key_pages = blk_pages;
   w.num_pages = a.num_pages;
   w.bt_row = a.block_tables + (size_t)b * a.stride;
   w.page_elems = (size_t)a.num_kv_heads * kPage * D;
   w.ktile = a.kpool + (size_t)kvh * kPage * D;
   w.vtile = a.vpool + (size_t)kvh * kPage * D;
-  // pair-mixed rows: QK row r of MFMA j is page r / 8, slot 8 ((r / 4) % 2) + 4 j + r % 4,
-  // so lane group grp ends up with slots 8 (grp % 2) + 0..7 of page grp / 2 for PV
-  w.koff = (uint32_t)((8 * ((r >> 2) & 1) + (r & 3)) * D + (D / 4) * grp);
-  w.voff = (uint32_t)(r * kPage + 8 * (grp & 1));
-  w.k_second = (r >> 3) != 0;
-  w.v_second = (grp >> 1) != 0;
-  const int qdim0 = (D / 4) * grp, qdim_step = 8;
-  // the softmax needs sl2 > 0: a negative scale is moved into the query
-  // (exact sign flips), and a zero scale is the same as a zero query
   const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
   const bool qzero = a.scale_log2 == 0.f;
   w.sl2 = qzero ? 1.f : fabsf(a.scale_log2);
@@ -380,21 +351,89 @@ __global__ __launch_bounds__(256, prefill_occupancy<D>()) void prefill_kernel(Pr
 #pragma unroll
   for (int g = 0; g < RG; ++g) {
     const int rho = rho0 + 16 * g + r;
-    valid[g] = rho < rows;
-    const int t = (valid[g] ? rho : rho_last) / G;    // chunk token of this lane's row
+    valid[g] = active && rho < rows;
+    const int t = (valid[g] ? rho : rho_last) / G;
     const int h = (valid[g] ? rho : rho_last) - t * G;
     w.pos[g] = ch.c + t;
     qrow[g] = ((size_t)(ch.r0 + t) * a.num_q_heads + (size_t)kvh * G + h) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      w.qf[g][kk] = as_bf16x8((valid[g] && !qzero) ? *(const u32x4*)(a.q + qrow[g] + qdim0 + qdim_step * kk) ^ qflip
+      w.qf[g][kk] = as_bf16x8((valid[g] && !qzero) ? *(const u32x4*)(a.q + qrow[g] + (D / 4) * grp + 8 * kk) ^ qflip
                                                     : u32x4{0u, 0u, 0u, 0u});
   }
+
+  // this thread's chunks of a pair: global element offsets within the page
+  // tile, page of the pair, and LDS byte offsets (operand order)
+  uint32_t kg[NPT], vg[NPT], kl[NPT], vl[NPT];
+  bool kp2[NPT], vp2[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const int c = tid + 256 * i;                       // chunk of the pair's K (or V)
+    const int p = c / (2 * D);                         // 2 D chunks per page (16 rows x D / 8)
+    const int ci = c - p * 2 * D;
+    {  // K: row s, 8-dim chunk cc
+      const int s = ci / (D / 8);
+      const int cc = ci - s * (D / 8);
+      const int j = (s >> 2) & 1;
+      const int rr = 8 * p + 4 * (s >> 3) + (s & 3);
+      const int gg = cc / KK;
+      const int kk = cc - gg * KK;
+      kg[i] = (uint32_t)(s * D + 8 * cc);
+      kl[i] = (uint32_t)(((j * KK + kk) * 64 + rr + 16 * gg) * 16);
+      kp2[i] = p != 0;
+    }
+    {  // V: head dim dd, 8-slot half hh
+      const int dd = ci >> 1;
+      const int hh = ci & 1;
+      const int mt = dd >> 4;
+      const int rr = dd & 15;
+      const int gg = 2 * p + hh;
+      vg[i] = (uint32_t)(dd * kPage + 8 * hh);
+      vl[i] = (uint32_t)(KB + (mt * 64 + rr + 16 * gg) * 16);
+      vp2[i] = p != 0;
+    }
+  }
+  u32x4 sk[NPT], sv[NPT];
+  auto gload = [&](int pr) {
+    const int pa = clamp_pid(w, 2 * pr);
+    const int pb = clamp_pid(w, min(2 * pr + 1, blk_pages - 1));
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      sk[i] = *(const u32x4*)(w.ktile + (size_t)(kp2[i] ? pb : pa) * w.page_elems + kg[i]);
+      sv[i] = *(const u32x4*)(w.vtile + (size_t)(vp2[i] ? pb : pa) * w.page_elems + vg[i]);
+    }
+  };
+  auto lstore = [&](int bufi) {
+    char* base = lds + bufi * PB;
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      *(u32x4*)(base + kl[i]) = sk[i];
+      *(u32x4*)(base + vl[i]) = sv[i];
+    }
+  };
 
   SoftmaxState<D> st[RG];
 #pragma unroll
   for (int g = 0; g < RG; ++g) init_state(st[g]);
-  prefill_stream(w, (w.key_pages + 1) >> 1, st, grp);
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int pr = 0; pr < npairs; ++pr) {
+    if (pr + 1 < npairs) gload(pr + 1);
+    if (active && 32 * pr <= w.last_pos) {
+      const char* base = lds + (pr & 1) * PB;
+      PrefillPair<D> buf;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) buf.k[j][kk] = *(const u32x4*)(base + ((j * KK + kk) * 64 + lane) * 16);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) buf.v[mt] = *(const u32x4*)(base + KB + (mt * 64 + lane) * 16);
+      prefill_compute(w, buf, pr, st, grp);
+    }
+    if (pr + 1 < npairs) lstore((pr + 1) & 1);
+    __syncthreads();
+  }
 #pragma unroll
   for (int g = 0; g < RG; ++g) {
     float l = st[g].l;
