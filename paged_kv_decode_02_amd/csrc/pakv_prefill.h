@@ -289,18 +289,19 @@ __host__ __device__ constexpr int prefill_block_rows() { return 64 * prefill_row
 // Grid: KV head fastest, then sequence, then row block from the last one
 // down, so the blocks that see the most keys start first. Wave w of a block
 // takes rows w * 32 .. w * 32 + 31 in two groups of 16. The 4 waves share
-// every K/V tile: per page pair the workgroup loads K and V once (coalesced 16-byte
+// every K/V tile: per page pair the workgroup loads K and V once (16-byte
 // loads, each thread its share), stores them to LDS in matrix-core operand
-// order (chunk (MFMA j, k-step kk or dim tile mt, lane) at a lane-linear
-// address, so the waves' 16-byte LDS reads are conflict-free), and every
-// wave reads its operands from there. Two LDS buffers: the next pair's
+// order (piece (MFMA j, k-step kk or dim tile mt, lane) at slot
+// (j KK + kk or mt) * 64 + lane, so both the stores and the waves' 16-byte
+// operand reads are lane-linear and free of bank conflicts), and every wave
+// reads its operands from there. Two LDS buffers: the next pair's
 // global loads are in flight while the current pair computes; one barrier
 // per pair.
 template <int D>
 struct PrefillLds {
   static constexpr int kKBytes = 2 * kPage * D * 2;     // K of a pair (two pages)
   static constexpr int kPairBytes = 2 * kKBytes;        // K and V
-  static constexpr int kPerThread = (4 * D) / 256;      // 16-byte K (and V) chunks per thread
+  static constexpr int kPerThread = (4 * D) / 256;      // 16-byte K (and V) pieces per thread
 };
 
 template <int D>
@@ -362,35 +363,31 @@ __global__ __launch_bounds__(256, prefill_occupancy<D>()) void prefill_kernel(Pr
                                                     : u32x4{0u, 0u, 0u, 0u});
   }
 
-  // this thread's chunks of a pair: global element offsets within the page
-  // tile, page of the pair, and LDS byte offsets (operand order)
+  // this thread's 16-byte pieces of a pair: LDS slot tid + 256 i of the K
+  // (and of the V) operand area, so that the stores are lane-linear; the
+  // piece it loads is the one the matrix core wants there
   uint32_t kg[NPT], vg[NPT], kl[NPT], vl[NPT];
   bool kp2[NPT], vp2[NPT];
 #pragma unroll
   for (int i = 0; i < NPT; ++i) {
-    const int c = tid + 256 * i;                       // chunk of the pair's K (or V)
-    const int p = c / (2 * D);                         // 2 D chunks per page (16 rows x D / 8)
-    const int ci = c - p * 2 * D;
-    {  // K: row s, 8-dim chunk cc
-      const int s = ci / (D / 8);
-      const int cc = ci - s * (D / 8);
-      const int j = (s >> 2) & 1;
-      const int rr = 8 * p + 4 * (s >> 3) + (s & 3);
-      const int gg = cc / KK;
-      const int kk = cc - gg * KK;
-      kg[i] = (uint32_t)(s * D + 8 * cc);
-      kl[i] = (uint32_t)(((j * KK + kk) * 64 + rr + 16 * gg) * 16);
-      kp2[i] = p != 0;
+    const int widx = tid + 256 * i;                    // operand slot: (MFMA / tile, lane)
+    const int ln = widx & 63;
+    const int lr = ln & 15;
+    const int lg = ln >> 4;
+    {  // K: MFMA j, k-step kk; QK row lr = page lr / 8, slot 8 ((lr / 4) % 2) + 4 j + lr % 4
+      const int jk = widx >> 6;
+      const int j = jk / KK;
+      const int kk = jk - j * KK;
+      const int slot = 8 * ((lr >> 2) & 1) + 4 * j + (lr & 3);
+      kg[i] = (uint32_t)(slot * D + (D / 4) * lg + 8 * kk);
+      kl[i] = (uint32_t)(widx * 16);
+      kp2[i] = (lr >> 3) != 0;
     }
-    {  // V: head dim dd, 8-slot half hh
-      const int dd = ci >> 1;
-      const int hh = ci & 1;
-      const int mt = dd >> 4;
-      const int rr = dd & 15;
-      const int gg = 2 * p + hh;
-      vg[i] = (uint32_t)(dd * kPage + 8 * hh);
-      vl[i] = (uint32_t)(KB + (mt * 64 + rr + 16 * gg) * 16);
-      vp2[i] = p != 0;
+    {  // V: head-dim tile mt; row 16 mt + lr, slots 8 (lg % 2) .. + 7 of page lg / 2
+      const int mt = widx >> 6;
+      vg[i] = (uint32_t)((16 * mt + lr) * kPage + 8 * (lg & 1));
+      vl[i] = (uint32_t)(KB + widx * 16);
+      vp2[i] = (lg >> 1) != 0;
     }
   }
   u32x4 sk[NPT], sv[NPT];
