@@ -49,7 +49,6 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 int split_pages(int d) { return d == 64 ? PAKV_SPLIT_PAGES_D64 : PAKV_SPLIT_PAGES_D128; }
-int waves(int d) { return d == 64 ? PAKV_WAVES_D64 : PAKV_WAVES_D128; }
 
 int64_t splits_for(int d, int32_t max_pages_per_seq) {
   const int64_t sp = split_pages(d);
@@ -100,10 +99,16 @@ struct LaunchTimer {
     rec.kind = kind;
     rec.start = take_event();
     rec.stop = take_event();
-    if (rec.start) (void)hipEventRecord(rec.start, stream);
+    if (!rec.start || !rec.stop) {   // keep whichever event was made for later
+      if (rec.start) g_free_events.push_back(rec.start);
+      if (rec.stop) g_free_events.push_back(rec.stop);
+      rec.start = rec.stop = nullptr;
+      return;
+    }
+    (void)hipEventRecord(rec.start, stream);
   }
   ~LaunchTimer() {
-    if (!g_profiling || !rec.start || !rec.stop) return;
+    if (!g_profiling || !rec.start) return;
     (void)hipEventRecord(rec.stop, stream);
     g_records.push_back(rec);
   }
