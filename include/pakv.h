@@ -167,8 +167,12 @@ pa_status pa_decode_append(const pa_pool* pool, const void* q, const void* k_new
  * and the largest splits of the longest sequences start last. A plan lists
  * only the splits that exist, largest first (page count descending; ties in
  * sequence order, then split order; a sequence with an empty context keeps
- * one item, last, which writes its zero output). Serving code knows its
- * context lengths on the host, and one plan serves every layer of a step.
+ * one item, last, which writes its zero output). When the whole grid fits
+ * the device at once (items x num_kv_heads <= 256 CUs x the decode
+ * workgroups a CU holds: 4 at head_dim 64, 2 at 128), every other tier of 32
+ * items (the CUs of one XCD) is reversed, so that each CU's items pair large
+ * with small. Serving code knows its context lengths on the host, and one
+ * plan serves every layer of a step.
  *
  * pa_decode_plan_capacity: items a plan may need for these sizes
  * (num_seqs * splits per sequence), or -1 when the sizes are out of range

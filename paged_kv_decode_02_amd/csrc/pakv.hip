@@ -43,12 +43,20 @@ namespace {
 constexpr int kMaxGroup = 16;   // query heads per KV head: the 16 MFMA columns
 constexpr int kProfileKinds = 5;  // decode, merge, append, chunk write, prefill
 constexpr int64_t kPlanMaxSeqs = 1 << 20;   // plan items pack b in 20 bits
+// MI355X geometry used by the launch plan's ordering (not by correctness)
+constexpr int kDeviceCUs = 256;
+constexpr int kCUsPerXCD = 32;
 constexpr int64_t kPlanMaxSplits = 1 << 11; // and the split in the 11 above them
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 int split_pages(int d) { return d == 64 ? PAKV_SPLIT_PAGES_D64 : PAKV_SPLIT_PAGES_D128; }
+
+// decode workgroups one CU holds at once (waves per SIMD x 4 SIMDs / waves per workgroup)
+int decode_wgs_per_cu(int d) {
+  return pakv::occupancy(d) * 4 / (d == 64 ? PAKV_WAVES_D64 : PAKV_WAVES_D128);
+}
 
 int64_t splits_for(int d, int32_t max_pages_per_seq) {
   const int64_t sp = split_pages(d);
@@ -357,6 +365,16 @@ pa_status pa_decode_plan(const pa_pool* pool, const int32_t* context_lens_host, 
       const int64_t pg = std::min<int64_t>(pages - s * sp, sp);
       plan[start[pg]++] = static_cast<int32_t>(static_cast<uint32_t>(b) | (static_cast<uint32_t>(s) << 20));
     }
+  }
+  // A grid the device holds all at once starts every workgroup together, and
+  // the workgroups reach the 8 XCDs round-robin, then a CU of their XCD in
+  // order: each CU gets items t, t + 32, t + 64, ... of its XCD's sequence.
+  // Reversing every other tier of 32 items pairs the large ones with small
+  // ones on each CU instead of stacking the large ones.
+  const int64_t resident = static_cast<int64_t>(kDeviceCUs) * decode_wgs_per_cu(pool->head_dim);
+  if (total * pool->num_kv_heads <= resident) {
+    for (int64_t t0 = kCUsPerXCD; t0 < total; t0 += 2 * kCUsPerXCD)
+      std::reverse(plan + t0, plan + std::min<int64_t>(t0 + kCUsPerXCD, total));
   }
   *num_items = static_cast<int32_t>(total);
   return PA_OK;

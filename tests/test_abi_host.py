@@ -160,9 +160,11 @@ def test_profile_and_status_strings():
 
 # ---- launch plan (pure host code)
 
-def expected_plan(ctx, stride, split_pages=64):
+def expected_plan(ctx, stride, split_pages=64, kv_heads=8, wgs_per_cu=4):
     """Every (sequence, split) that exists, sorted by page count descending, then
-    sequence, then split; an empty context keeps one zero-page item."""
+    sequence, then split; an empty context keeps one zero-page item. When the
+    grid fits the device at once (items x kv heads <= 256 CUs x workgroups per
+    CU), every other tier of 32 items is reversed."""
     items = []
     for b, n in enumerate(ctx):
         n = min(max(int(n), 0), stride * 16)
@@ -173,7 +175,11 @@ def expected_plan(ctx, stride, split_pages=64):
         for s in range((pages + split_pages - 1) // split_pages):
             items.append((min(pages - s * split_pages, split_pages), b, s))
     items.sort(key=lambda t: (-t[0], t[1], t[2]))
-    return [b | (s << 20) for _, b, s in items]
+    out = [b | (s << 20) for _, b, s in items]
+    if len(out) * kv_heads <= 256 * wgs_per_cu:
+        for t0 in range(32, len(out), 64):
+            out[t0:t0 + 32] = out[t0:t0 + 32][::-1]
+    return out
 
 
 def test_plan_order_and_clamping():
@@ -211,7 +217,7 @@ def test_plan_validation():
     assert L.pa_decode_plan(h, ctx.ctypes.data, 3, 400, buf.ctypes.data, 6, ctypes.byref(n)) == INVALID
     assert L.pa_decode_plan(h, ctx.ctypes.data, 3, 400, buf.ctypes.data, 8, ctypes.byref(n)) == OK
     assert n.value == 7
-    assert buf[:7].tolist() == expected_plan(ctx, 400)
+    assert buf[:7].tolist() == expected_plan(ctx, 400, kv_heads=8, wgs_per_cu=2)
     assert L.pa_decode_plan(h, ctx.ctypes.data, 0, 400, None, 0, ctypes.byref(n)) == OK and n.value == 0
     L.pa_pool_destroy(h)
 
@@ -262,3 +268,20 @@ def test_prefill_and_write_validation():
     assert L.pa_kv_write(h, P, P, 1, 4, 4, P, P, 0, P, None) == INVALID
     assert L.pa_kv_write(h, None, None, 0, 4, 4, None, None, 2, None, None) == OK
     L.pa_pool_destroy(h)
+
+
+def test_plan_tiers_reversed_only_when_the_grid_fits_at_once():
+    import numpy as np
+    h = make_pool(d=64)                       # 8 KV heads, 4 decode workgroups per CU: 1024 resident
+    pool = type("P", (), {"handle": h})()
+    rng = np.random.default_rng(3)
+    small = rng.integers(1, 1025, 100).astype(np.int32)     # 100 items x 8 = 800: one round
+    got = B.decode_plan(pool, small, 64)
+    assert got.tolist() == expected_plan(small, 64)
+    plain = sorted(range(100), key=lambda b: (-(-(-int(small[b]) // 16)), b))
+    assert got[:32].tolist() == plain[:32] and got[32:64].tolist() == plain[32:64][::-1]
+    assert got[64:96].tolist() == plain[64:96] and got[96:].tolist() == plain[96:][::-1]
+    large = rng.integers(1, 1025, 200).astype(np.int32)     # 200 x 8 = 1600: several rounds
+    got = B.decode_plan(pool, large, 64)
+    assert got.tolist() == sorted(range(200), key=lambda b: (-(-(-int(large[b]) // 16)), b))
+    B.lib().pa_pool_destroy(h)
