@@ -526,8 +526,9 @@ __global__ __launch_bounds__(64 * W, occupancy(D)) void decode_split_kernel(Deco
 }
 
 // One wave per (sequence, query head): combine the splits of sequences that
-// have more than one, in split order. Lane i holds split i's (m, l) so all of
-// them arrive with one load; the partial outputs are read four splits at a time.
+// have more than one, in split order. Lane i holds split i's (m, l); they are
+// loaded together with the context length, so the partial outputs (read four
+// splits at a time) are two dependent loads away from the start.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -546,13 +547,21 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(DecodeArgs a, int spl
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= a.num_seqs * a.num_q_heads) return;
   const int b = item / a.num_q_heads;
-  const int n = clamp_ctx(a.ctx[b], a.stride);
-  const int nsplit = (n + split_tokens - 1) / split_tokens;
-  if (nsplit <= 1) return;
   const float* ml = a.ws_ml + (size_t)item * a.s_max * 2;
   const float* acc = a.ws_acc + (size_t)item * a.s_max * D;
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < nsplit; s0 += 64)
+  // the context length and the first 64 splits' (m, l) are loaded together;
+  // lanes past the sequence's split count drop theirs
+  const int ctx_b = a.ctx[b];
+  float m0 = -INFINITY, l0 = 0.f;
+  if (lane < a.s_max) {
+    m0 = ml[2 * lane];
+    l0 = ml[2 * lane + 1];
+  }
+  const int n = clamp_ctx(ctx_b, a.stride);
+  const int nsplit = (n + split_tokens - 1) / split_tokens;
+  if (nsplit <= 1) return;
+  float M = lane < nsplit ? m0 : -INFINITY;
+  for (int s0 = 64; s0 < nsplit; s0 += 64)
     if (s0 + lane < nsplit) M = fmaxf(M, ml[2 * (s0 + lane)]);
   M = wave_max(M);
   float L = 0.f;
@@ -563,8 +572,10 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(DecodeArgs a, int spl
     const int cnt = min(64, nsplit - s0);
     float c = 0.f;
     if (lane < cnt) {
-      c = __builtin_amdgcn_exp2f(ml[2 * (s0 + lane)] - M);
-      L += c * ml[2 * (s0 + lane) + 1];
+      const float mm = s0 == 0 ? m0 : ml[2 * (s0 + lane)];
+      const float ll = s0 == 0 ? l0 : ml[2 * (s0 + lane) + 1];
+      c = __builtin_amdgcn_exp2f(mm - M);
+      L += c * ll;
     }
     int j = 0;
     for (; j + 4 <= cnt; j += 4) {
