@@ -118,6 +118,7 @@ EDGE_CASES = [
     ("group8_d128", [300, 1100], 8, 1, 128),
     ("group16_d128", [65, 1500], 32, 2, 128),
     ("long_d128", [16384, 12345], 28, 4, 128),
+    ("beyond_64_splits_d64", [70000, 3, 65537], 32, 8, 64),
     ("ragged_many", list(np.random.default_rng(4).integers(0, 700, 37)), 32, 8, 64),
 ]
 

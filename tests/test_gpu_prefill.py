@@ -47,6 +47,8 @@ CASES = [
     ("g16_d64", 32, 2, 64, [9], [70]),
     ("g1_d64", 8, 8, 64, [40, 0], [25, 48]),
     ("g8_d128", 8, 1, 128, [15], [49]),
+    ("g16_d128", 32, 2, 128, [0, 40], [33, 90]),
+    ("g2_d64", 4, 2, 64, [3], [130]),
 ]
 
 
