@@ -279,9 +279,11 @@ __device__ __forceinline__ void prefill_compute(const PrefillWave<D, RG>& w, Pre
 // Two groups of 16 rows per wave: every K/V operand loaded feeds both.
 template <int D>
 __host__ __device__ constexpr int prefill_row_groups() { return 2; }
-// Waves per SIMD the register budget allows (185 / 320 registers per lane).
+// Waves per SIMD: 4 at d = 64 (128 registers per lane, a few spilled; more
+// waves overlap one wave's softmax with another's matrix-core work and
+// measured faster than 2 or 3), 1 at d = 128 (2 measured the same).
 template <int D>
-__host__ __device__ constexpr int prefill_occupancy() { return D == 64 ? 2 : 1; }
+__host__ __device__ constexpr int prefill_occupancy() { return D == 64 ? 4 : 1; }
 // rows per workgroup: 4 waves x 16 rows x row groups
 template <int D>
 __host__ __device__ constexpr int prefill_block_rows() { return 64 * prefill_row_groups<D>(); }
