@@ -31,13 +31,18 @@
  * Memory layout (all device memory is owned by the caller; the library never
  * allocates, frees or synchronises, and queues all work on the caller's
  * stream):
- *  - K pool: BF16 [num_pages][num_kv_heads][16][head_dim]
- *            element (p, g, slot, i) at ((p * Hkv + g) * 16 + slot) * d + i
+ *  - K pool: BF16 [num_pages][num_kv_heads][head_dim / 32][16][32]
+ *            element (p, g, slot, i) at
+ *            ((p * Hkv + g) * 16 * d) + (i / 32) * 512 + slot * 32 + i % 32
  *  - V pool: BF16 [num_pages][num_kv_heads][head_dim][16]
  *            element (p, g, slot, i) at ((p * Hkv + g) * d + i) * 16 + slot
- *    One physical page id indexes both pools. The V pool keeps the 16 slots of
- *    each dimension together so that a decode lane's 16-byte load is exactly
- *    one matrix-core operand (8 consecutive tokens of one dimension).
+ *    One physical page id indexes both pools, and each (page, KV head) tile is
+ *    16 * d contiguous elements in both. Inside a K tile the dimensions come
+ *    in slabs of 32: a slab holds 64 bytes of every slot, so the 16-byte
+ *    operand pieces one matrix-core K-step needs from 16 tokens fill whole
+ *    128-byte cache lines. The V pool keeps the 16 slots of each dimension
+ *    together so that a decode lane's 16-byte load is exactly one
+ *    matrix-core operand (8 consecutive tokens of one dimension).
  *  - q: BF16 [num_seqs][num_q_heads][head_dim]
  *  - out: FP32 [num_seqs][num_q_heads][head_dim]
  *  - k_new, v_new: BF16 [num_seqs][num_kv_heads][head_dim]

@@ -4,10 +4,10 @@ Only the tests, the smoke check and the benchmark's CPU-baseline leg may
 import this package. The product path never does.
 """
 
-from .paged_attention import (PAGE_SIZE, attend_one_head, bf16_bits_to_f64,
-                              decode_attention, gather_sequence, kv_append, kv_write,
-                              prefill_attention)
+from .paged_attention import (K_SLAB, PAGE_SIZE, attend_one_head, bf16_bits_to_f64,
+                              decode_attention, gather_sequence, k_slot_row, kv_append,
+                              kv_write, prefill_attention, set_k_slot_row)
 
-__all__ = ["PAGE_SIZE", "attend_one_head", "bf16_bits_to_f64",
-           "decode_attention", "gather_sequence", "kv_append", "kv_write",
-           "prefill_attention"]
+__all__ = ["K_SLAB", "PAGE_SIZE", "attend_one_head", "bf16_bits_to_f64",
+           "decode_attention", "gather_sequence", "k_slot_row", "kv_append", "kv_write",
+           "prefill_attention", "set_k_slot_row"]

@@ -36,9 +36,11 @@ Readings taken where the pages are silent:
   the oracle is the plain definition: gather, scores, two-pass softmax,
   weighted sum of V, all in float64.
 * Pool layout inside a page (the pages give none): K is
-  ``[num_pages][num_kv_heads][16][head_dim]`` and V is
+  ``[num_pages][num_kv_heads][head_dim / 32][16][32]`` (the head dimensions
+  in slabs of 32, each slab holding all 16 slots) and V is
   ``[num_pages][num_kv_heads][head_dim][16]`` (V stores the 16 slots of each
-  dimension together). One physical page id indexes both.
+  dimension together). One physical page id indexes both. The oracle takes
+  the K pool as that 5-D array and V as the 4-D one.
 * ``ctx_len == 0`` gives an all-zero output. Slots at or beyond ``ctx_len``
   and pages a sequence does not reference may hold any bits, NaN included;
   they never contribute.
@@ -51,6 +53,7 @@ from __future__ import annotations
 import numpy as np
 
 PAGE_SIZE = 16  # tokens per physical page [samir-course]
+K_SLAB = 32     # head dimensions per K slab (pool layout reading above)
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -65,6 +68,23 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
         return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def k_slot_row(k_pool: np.ndarray, physical: int, slot: int) -> np.ndarray:
+    """The K values of one slot of one page, all KV heads: ``[Hkv][d]`` bits.
+
+    Dimension ``i`` of the row lies in slab ``i // 32`` at column ``i % 32``,
+    so concatenating the slabs in order gives the row.
+    """
+    num_kv_heads, slabs = k_pool.shape[1], k_pool.shape[2]
+    return k_pool[physical, :, :, slot, :].reshape(num_kv_heads, slabs * K_SLAB)
+
+
+def set_k_slot_row(k_pool: np.ndarray, physical: int, slot: int, rows: np.ndarray) -> None:
+    """Store ``rows`` (``[Hkv][d]`` bits) into one slot of one page, slab by
+    slab (the inverse of ``k_slot_row``)."""
+    rows = np.asarray(rows, dtype=np.uint16)
+    k_pool[physical, :, :, slot, :] = rows.reshape(rows.shape[0], -1, K_SLAB)
+
+
 def gather_sequence(k_pool: np.ndarray, v_pool: np.ndarray,
                     block_table_row: np.ndarray, ctx_len: int):
     """Copy one sequence's cached tokens out of the pages into contiguous
@@ -76,8 +96,10 @@ def gather_sequence(k_pool: np.ndarray, v_pool: np.ndarray,
     pre-paging cache.
     """
     n = int(ctx_len)
-    num_pages, num_kv_heads, page, head_dim = k_pool.shape
-    assert page == PAGE_SIZE and v_pool.shape == (num_pages, num_kv_heads, head_dim, PAGE_SIZE)
+    num_pages, num_kv_heads, slabs, page, width = k_pool.shape
+    head_dim = slabs * width
+    assert page == PAGE_SIZE and width == K_SLAB
+    assert v_pool.shape == (num_pages, num_kv_heads, head_dim, PAGE_SIZE)
     kc = np.empty((n, num_kv_heads, head_dim), dtype=np.float64)
     vc = np.empty((n, num_kv_heads, head_dim), dtype=np.float64)
     for t in range(n):
@@ -85,7 +107,7 @@ def gather_sequence(k_pool: np.ndarray, v_pool: np.ndarray,
         slot = t % PAGE_SIZE
         physical = int(block_table_row[logical_page])
         assert 0 <= physical < num_pages, "block table names a page outside the pool"
-        kc[t] = bf16_bits_to_f64(k_pool[physical, :, slot, :])
+        kc[t] = bf16_bits_to_f64(k_slot_row(k_pool, physical, slot))
         vc[t] = bf16_bits_to_f64(v_pool[physical, :, :, slot])
     return kc, vc
 
@@ -110,7 +132,7 @@ def decode_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
     """Decode-step grouped-query attention over paged K/V, in float64.
 
     q            uint16 (BF16 bits) ``[B][Hq][d]``, one new query per sequence
-    k_pool       uint16 ``[P][Hkv][16][d]``
+    k_pool       uint16 ``[P][Hkv][d/32][16][32]``
     v_pool       uint16 ``[P][Hkv][d][16]``
     block_tables int ``[B][stride]`` physical page of each logical page
     ctx_lens     int ``[B]`` cached tokens to attend over (0 gives zeros)
@@ -158,9 +180,8 @@ def kv_append(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray,
             continue
         physical = int(block_tables[b][pos // PAGE_SIZE])
         slot = pos % PAGE_SIZE
-        for g in range(k_new.shape[1]):
-            k_out[physical, g, slot, :] = k_new[b, g, :]
-            v_out[physical, g, :, slot] = v_new[b, g, :]
+        set_k_slot_row(k_out, physical, slot, k_new[b])
+        v_out[physical, :, :, slot] = v_new[b]
     return k_out, v_out
 
 
@@ -182,7 +203,7 @@ def kv_write(k_pool: np.ndarray, v_pool: np.ndarray, k_rows: np.ndarray,
             pos = int(ctx_before[b]) + row - int(query_start[b])
             physical = int(block_tables[b][pos // PAGE_SIZE])
             slot = pos % PAGE_SIZE
-            k_out[physical, :, slot, :] = k_rows[row]
+            set_k_slot_row(k_out, physical, slot, k_rows[row])
             v_out[physical, :, :, slot] = v_rows[row]
     return k_out, v_out
 

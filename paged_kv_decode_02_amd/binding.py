@@ -160,12 +160,16 @@ def _bf16_types():
 
 
 class Pool:
-    """A caller-owned K/V page pool: K ``[P][Hkv][16][d]``, V ``[P][Hkv][d][16]``."""
+    """A caller-owned K/V page pool: K ``[P][Hkv][d/32][16][32]``, V
+    ``[P][Hkv][d][16]``."""
 
     def __init__(self, k_pages, v_pages):
-        _need(k_pages, "k_pages", _bf16_types(), 4)
+        _need(k_pages, "k_pages", _bf16_types(), 5)
         _need(v_pages, "v_pages", _bf16_types(), 4)
-        num_pages, hkv, page, d = k_pages.shape
+        num_pages, hkv, slabs, page, width = k_pages.shape
+        d = slabs * width
+        if width != 32:
+            raise ValueError(f"k_pages shape {tuple(k_pages.shape)}: the last dim holds 32 head dims")
         if tuple(v_pages.shape) != (num_pages, hkv, d, page):
             raise ValueError(f"v_pages shape {tuple(v_pages.shape)} does not match K {tuple(k_pages.shape)}")
         handle = ctypes.c_void_p()

@@ -33,7 +33,8 @@
 // Lane roles (lane = 0..63, r = lane % 16, grp = lane / 16):
 //   QK A operand   row r = token: page (r / 8) of the pair,
 //                  slot 8 * ((r / 4) % 2) + 4 * j + r % 4 for MFMA j = 0, 1;
-//                  k = head dims (D / 4) * grp + 8 * kk + 0..7
+//                  k = head dims 8 * grp + 32 * kk + 0..7 (K slab kk: one
+//                  load instruction fills 8 whole 128-byte lines)
 //   QK result      lane holds S for head r, tokens 8 * grp + 4 * j + i
 //   PV B operand   same lane, same 8 tokens (k = 8 * grp + e)
 //   PV A operand   row = head dim 16 * mt + r, tokens 8 * grp + 0..7 ->
@@ -47,6 +48,13 @@
 namespace pakv {
 
 constexpr int kPage = 16;
+
+// Offset of element (slot t, dim e) inside one (page, KV head) K tile: the
+// dims come in slabs of 32, each holding 64 bytes of all 16 slots, so the
+// pieces one matrix-core K-step reads from 16 tokens are whole cache lines.
+__host__ __device__ constexpr int k_offset(int t, int e) {
+  return (e >> 5) * (kPage * 32) + t * 32 + (e & 31);
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -111,10 +119,11 @@ __host__ __device__ constexpr bool nt_k() { return D == 64; }
 template <int D>
 __host__ __device__ constexpr bool nt_v() { return true; }
 
-// Head dims held by lane group grp for QK k-step kk (8 consecutive dims);
-// the keys (A operand), the query (B operand) and the fused append use it.
+// Head dims held by lane group grp for QK k-step kk (8 consecutive dims):
+// k-step kk covers K slab kk. The keys (A operand), the query (B operand),
+// the fused append and the prefill use it.
 template <int D>
-__host__ __device__ constexpr int kdim(int grp, int kk) { return (D / 4) * grp + 8 * kk; }
+__host__ __device__ constexpr int kdim(int grp, int kk) { return 8 * grp + 32 * kk; }
 
 template <bool NT>
 __device__ __forceinline__ u32x4 ld_stream(const u32x4* p) {
@@ -164,7 +173,7 @@ __device__ __forceinline__ void issue_pair(const SplitCtx<D>& c, PairBuf<D>& buf
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) buf.k[j][kk] = ld_stream<nt_k<D>()>((const u32x4*)(kp + 4 * j * D + kdim<D>(0, kk)));
+    for (int kk = 0; kk < KK; ++kk) buf.k[j][kk] = ld_stream<nt_k<D>()>((const u32x4*)(kp + k_offset(4 * j, kdim<D>(0, kk))));
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) buf.v[mt] = ld_stream<nt_v<D>()>((const u32x4*)(vp + mt * 16 * kPage));
   // keep later pairs' loads and this pair's math in program order, so the
@@ -303,7 +312,7 @@ __device__ __forceinline__ void make_split_ctx(const DecodeArgs& a, int b, int k
     for (int kk = 0; kk < KK; ++kk) c.qf[kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   }
   c.page_elems = (size_t)a.num_kv_heads * TILE;
-  const int koff = (8 * ((r >> 2) & 1) + (r & 3)) * D + kdim<D>(grp, 0);
+  const int koff = k_offset(8 * ((r >> 2) & 1) + (r & 3), kdim<D>(grp, 0));
   const int voff = r * kPage + 8 * (grp & 1);
   c.k_second = (r >> 3) != 0;
   c.v_second = (grp >> 1) != 0;
@@ -358,9 +367,9 @@ __device__ __forceinline__ void append_unattended(const DecodeArgs& a, int b, in
   const size_t tile = (size_t)pid * a.num_kv_heads + kvh;
   const uint16_t* kn = a.k_new + ((size_t)b * a.num_kv_heads + kvh) * D;
   const uint16_t* vn = a.v_new + ((size_t)b * a.num_kv_heads + kvh) * D;
-  uint16_t* kdst = const_cast<uint16_t*>(a.kpool) + (tile * kPage + slot) * D;
+  uint16_t* ktile = const_cast<uint16_t*>(a.kpool) + tile * kPage * D;
   uint16_t* vdst = const_cast<uint16_t*>(a.vpool) + tile * D * kPage + slot;
-  if (lane < D / 8) *(u32x4*)(kdst + 8 * lane) = *(const u32x4*)(kn + 8 * lane);
+  if (lane < D / 8) *(u32x4*)(ktile + k_offset(slot, 8 * lane)) = *(const u32x4*)(kn + 8 * lane);
   write_v_column<D>(vdst - slot, vn, slot, lane);
 }
 
@@ -383,10 +392,10 @@ __device__ __forceinline__ void append_by_reader(const DecodeArgs& a, int b, int
   const uint16_t* vn = a.v_new + ((size_t)b * a.num_kv_heads + kvh) * D;
   // K: the QK row of this token is r = 8 * page-in-pair + 4 * (slot / 8) + slot % 4
   if (r == 8 * p_in_pair + 4 * (slot >> 3) + (slot & 3)) {
-    uint16_t* kdst = const_cast<uint16_t*>(a.kpool) + (tile * kPage + slot) * D;
+    uint16_t* ktile = const_cast<uint16_t*>(a.kpool) + tile * kPage * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      *(u32x4*)(kdst + kdim<D>(grp, kk)) = *(const u32x4*)(kn + kdim<D>(grp, kk));
+      *(u32x4*)(ktile + k_offset(slot, kdim<D>(grp, kk))) = *(const u32x4*)(kn + kdim<D>(grp, kk));
   }
   // V: the two lane groups 2 * page-in-pair and 2 * page-in-pair + 1 load the
   // two 16-byte halves of every 32-byte slot row of this page. They read their
@@ -624,7 +633,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   for (int c = t; c < H * (D / 8); c += 256) {
     const int g = c / (D / 8);
     const int part = c - g * (D / 8);
-    *(u32x4*)(a.kpool + ((tile0 + g) * kPage + slot) * D + 8 * part) =
+    *(u32x4*)(a.kpool + (tile0 + g) * kPage * D + k_offset(slot, 8 * part)) =
         *(const u32x4*)(kn + (size_t)g * D + 8 * part);
   }
   const int w = (slot & 7) >> 1;

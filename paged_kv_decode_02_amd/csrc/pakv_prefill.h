@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(WriteArgs a) {
     const int g = (e / (D / 8)) % H;
     const int slot = s0 + e / ((D / 8) * H);
     const size_t row = (size_t)(row_of_slot0 + slot);
-    *(u32x4*)(a.kpool + ((tile0 + g) * kPage + slot) * D + 8 * part) =
+    *(u32x4*)(a.kpool + (tile0 + g) * kPage * D + k_offset(slot, 8 * part)) =
         *(const u32x4*)(a.k_rows + (row * H + g) * D + 8 * part);
   }
   // V: one slot row per (kv head, head dim)
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(256, prefill_occupancy<D>()) void prefill_kernel(Pr
     qrow[g] = ((size_t)(ch.r0 + t) * a.num_q_heads + (size_t)kvh * G + h) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      w.qf[g][kk] = as_bf16x8((valid[g] && !qzero) ? *(const u32x4*)(a.q + qrow[g] + (D / 4) * grp + 8 * kk) ^ qflip
+      w.qf[g][kk] = as_bf16x8((valid[g] && !qzero) ? *(const u32x4*)(a.q + qrow[g] + kdim<D>(grp, kk)) ^ qflip
                                                     : u32x4{0u, 0u, 0u, 0u});
   }
 
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(256, prefill_occupancy<D>()) void prefill_kernel(Pr
       const int j = jk / KK;
       const int kk = jk - j * KK;
       const int slot = 8 * ((lr >> 2) & 1) + 4 * j + (lr & 3);
-      kg[i] = (uint32_t)(slot * D + (D / 4) * lg + 8 * kk);
+      kg[i] = (uint32_t)k_offset(slot, kdim<D>(lg, kk));
       kl[i] = (uint32_t)(widx * 16);
       kp2[i] = (lr >> 3) != 0;
     }

@@ -19,7 +19,8 @@ a pool too large for the host can be regenerated there on its own:
   inverse-transform sampling of N(0, sigma^2), discretised to 2^16 levels.
 
 Pool layout (shared with the library's header): K is
-``[num_pages][Hkv][16][d]``, V is ``[num_pages][Hkv][d][16]``, BF16.
+``[num_pages][Hkv][d/32][16][32]`` (head dims in slabs of 32, each slab
+holding all 16 slots), V is ``[num_pages][Hkv][d][16]``, BF16.
 Slots that hold no token (tails of last pages, pages nobody references, and in
 append workloads the slot the new token will fill) are set to BF16 NaN
 (0x7FC0), so that reading them by mistake shows up in the output.
@@ -37,6 +38,7 @@ from typing import List, Optional
 import numpy as np
 
 PAGE = 16
+K_SLAB = 32          # head dims per K slab: K pool [page][kv_head][d/32][16][32]
 NAN_BITS = 0x7FC0
 MASK32 = 0xFFFFFFFF
 
@@ -172,9 +174,14 @@ class Workload:
 
     # -- pool contents
     def _slot_of(self, which: str, elem_in_page):
-        if which == "k":        # [Hkv][16][d]
-            return (elem_in_page // self.head_dim) % PAGE
+        if which == "k":        # [Hkv][d/32][16][32]
+            return (elem_in_page // K_SLAB) % PAGE
         return elem_in_page % PAGE  # [Hkv][d][16]
+
+    def _pool_shape(self, which: str, pages: int):
+        if which == "k":
+            return (pages, self.num_kv_heads, self.head_dim // K_SLAB, PAGE, K_SLAB)
+        return (pages, self.num_kv_heads, self.head_dim, PAGE)
 
     def pool_pages_bits(self, which: str, page_ids) -> np.ndarray:
         """Host copy of the listed physical pages, shaped like the pool."""
@@ -190,9 +197,7 @@ class Workload:
             v = values_np(self.seed, stream, idx, self.table())
             poison = slot[None, :] >= self.page_valid[ids][:, None]
             out[i0:i0 + ids.size] = np.where(poison, np.uint16(NAN_BITS), v)
-        if which == "k":
-            return out.reshape(page_ids.size, self.num_kv_heads, PAGE, self.head_dim)
-        return out.reshape(page_ids.size, self.num_kv_heads, self.head_dim, PAGE)
+        return out.reshape(self._pool_shape(which, page_ids.size))
 
     def pool_bits(self, which: str) -> np.ndarray:
         return self.pool_pages_bits(which, np.arange(self.num_pages))
@@ -218,9 +223,7 @@ class Workload:
             poison = slot >= valid[idx // e]
             pool[start:end] = torch.where(poison, nan, v)
             del idx, h, v, local, slot, poison
-        if which == "k":
-            return pool.view(self.num_pages, self.num_kv_heads, PAGE, self.head_dim)
-        return pool.view(self.num_pages, self.num_kv_heads, self.head_dim, PAGE)
+        return pool.view(self._pool_shape(which, self.num_pages))
 
     def sequence_pages(self, layer: int, b: int) -> np.ndarray:
         n = int(self.ctx_lens[b])

@@ -48,12 +48,27 @@ def random_bf16(rng, shape, sigma=1.0) -> np.ndarray:
     return f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32) * np.float32(sigma))
 
 
+def to_k_slabs(k_by_slot_pool: np.ndarray) -> np.ndarray:
+    """``[P][Hkv][16][d]`` (one row per slot) to the pool's K layout
+    ``[P][Hkv][d/32][16][32]``: dimension i of slot t goes to slab i // 32,
+    row t, column i % 32."""
+    p, h, page, d = k_by_slot_pool.shape
+    assert d % 32 == 0
+    return np.ascontiguousarray(k_by_slot_pool.reshape(p, h, page, d // 32, 32).transpose(0, 1, 3, 2, 4))
+
+
+def k_by_slot(k_pool: np.ndarray) -> np.ndarray:
+    """The inverse of ``to_k_slabs``: the K pool as ``[P][Hkv][16][d]``."""
+    p, h, slabs, page, width = k_pool.shape
+    return np.ascontiguousarray(k_pool.transpose(0, 1, 3, 2, 4)).reshape(p, h, page, slabs * width)
+
+
 def scatter_pages(kc_bits, vc_bits, ctx_lens, num_pages, rng, fill=NAN_BF16,
                   stride=None, pages_per_seq=None):
     """Place contiguous per-sequence K/V (``[B][n][Hkv][d]`` lists of uint16)
     into a pool at random physical pages. Unused slots and pages get ``fill``.
 
-    K pool ``[P][Hkv][16][d]``; V pool ``[P][Hkv][d][16]``.
+    K pool ``[P][Hkv][d/32][16][32]``; V pool ``[P][Hkv][d][16]``.
     Returns (k_pool, v_pool, block_tables).
     """
     num_seqs = len(ctx_lens)
@@ -77,7 +92,7 @@ def scatter_pages(kc_bits, vc_bits, ctx_lens, num_pages, rng, fill=NAN_BF16,
             p = bt[b, t // PAGE]
             k_pool[p, :, t % PAGE, :] = kc_bits[b][t]
             v_pool[p, :, :, t % PAGE] = vc_bits[b][t]
-    return k_pool, v_pool, bt
+    return to_k_slabs(k_pool), v_pool, bt
 
 
 def make_case(rng, num_seqs, hq, hkv, d, ctx_lens, extra_pages=5, sigma=1.0):
@@ -118,10 +133,10 @@ def pin_sdpa_library(o):
     KV heads repeated G times each (contiguous grouping, so repeat_interleave)."""
     import torch
     rng = np.random.default_rng(11)
-    for (hq, hkv, d, lens) in [(8, 2, 16, [1, 15, 16, 17, 40]),
-                               (6, 3, 8, [33, 2, 64]),
+    for (hq, hkv, d, lens) in [(8, 2, 64, [1, 15, 16, 17, 40]),
+                               (6, 3, 32, [33, 2, 64]),
                                (7, 1, 32, [5, 48]),
-                               (4, 4, 8, [31])]:
+                               (4, 4, 32, [31])]:
         q, kc, vc, k_pool, v_pool, bt, ctx = make_case(rng, len(lens), hq, hkv, d, lens)
         scale = np.float32(1.0 / math.sqrt(d)) * np.float32(1.5)
         out = o.decode_attention(q, k_pool, v_pool, bt, ctx, scale)
@@ -140,7 +155,7 @@ def pin_sdpa_library(o):
 def pin_ctx_one_returns_value(o):
     """A single cached token gets softmax weight 1: the output is that V row."""
     rng = np.random.default_rng(12)
-    q, kc, vc, k_pool, v_pool, bt, ctx = make_case(rng, 3, 8, 2, 16, [1, 1, 1])
+    q, kc, vc, k_pool, v_pool, bt, ctx = make_case(rng, 3, 8, 2, 32, [1, 1, 1])
     out = o.decode_attention(q, k_pool, v_pool, bt, ctx, np.float32(0.25))
     for b in range(3):
         for h in range(8):
@@ -151,7 +166,7 @@ def pin_ctx_one_returns_value(o):
 def pin_ctx_two_sigmoid(o):
     """Two tokens: the weight of token 0 is the logistic function of s0 - s1."""
     rng = np.random.default_rng(13)
-    q, kc, vc, k_pool, v_pool, bt, ctx = make_case(rng, 2, 4, 2, 8, [2, 2])
+    q, kc, vc, k_pool, v_pool, bt, ctx = make_case(rng, 2, 4, 2, 32, [2, 2])
     scale = np.float32(0.3)
     out = o.decode_attention(q, k_pool, v_pool, bt, ctx, scale)
     for b in range(2):
@@ -170,9 +185,9 @@ def pin_identical_keys_mean(o):
     """All keys equal: equal weights, the output is the mean of the V rows."""
     rng = np.random.default_rng(14)
     n = 37
-    q, kc, vc, k_pool, v_pool, bt, ctx = make_case(rng, 1, 4, 1, 16, [n])
-    row = random_bf16(rng, (1, 16))
-    kc_same = [np.broadcast_to(row, (n, 1, 16)).copy()]
+    q, kc, vc, k_pool, v_pool, bt, ctx = make_case(rng, 1, 4, 1, 32, [n])
+    row = random_bf16(rng, (1, 32))
+    kc_same = [np.broadcast_to(row, (n, 1, 32)).copy()]
     k_pool, v_pool, bt = scatter_pages(kc_same, vc, [n], 6, rng)
     out = o.decode_attention(q, k_pool, v_pool, bt, ctx, np.float32(0.7))
     ref = bits_to_f64_ref(vc[0][:, 0, :]).mean(axis=0)
@@ -184,7 +199,7 @@ def pin_zero_query_or_scale_mean(o):
     """q = 0 or scale = 0 makes every score 0: output is the mean of V."""
     rng = np.random.default_rng(15)
     lens = [20, 3]
-    q, kc, vc, k_pool, v_pool, bt, ctx = make_case(rng, 2, 6, 3, 8, lens)
+    q, kc, vc, k_pool, v_pool, bt, ctx = make_case(rng, 2, 6, 3, 32, lens)
     zero_q = np.zeros_like(q)
     for qq, sc in [(zero_q, np.float32(0.5)), (q, np.float32(0.0))]:
         out = o.decode_attention(qq, k_pool, v_pool, bt, ctx, sc)
@@ -198,8 +213,8 @@ def pin_value_ones_convex(o):
     """Softmax weights sum to one: all-ones V gives exactly 1 (to rounding)."""
     rng = np.random.default_rng(16)
     lens = [1, 16, 50]
-    q, kc, vc, k_pool, v_pool, bt, ctx = make_case(rng, 3, 4, 2, 8, lens)
-    ones = [np.full((n, 2, 8), 0x3F80, dtype=np.uint16) for n in lens]
+    q, kc, vc, k_pool, v_pool, bt, ctx = make_case(rng, 3, 4, 2, 32, lens)
+    ones = [np.full((n, 2, 32), 0x3F80, dtype=np.uint16) for n in lens]
     k_pool, v_pool, bt = scatter_pages(kc, ones, lens, 10, rng)
     out = o.decode_attention(q, k_pool, v_pool, bt, ctx, np.float32(0.4))
     _assert_close(out, np.ones_like(out), 1e-14, "V = 1")
@@ -209,7 +224,7 @@ def pin_hard_max(o):
     """With a huge scale one token dominates: exp of the others underflows to
     exactly 0 and the output equals that token's V row (needs the max shift)."""
     rng = np.random.default_rng(17)
-    n, d = 12, 8
+    n, d = 12, 32
     q = f32_to_bf16_bits(np.ones((1, 1, d), np.float32))
     kc_f = np.full((n, 1, d), -1.0, np.float32)
     kc_f[5] = 1.0
@@ -222,9 +237,9 @@ def pin_hard_max(o):
 
 def pin_ctx_zero_gives_zeros(o):
     rng = np.random.default_rng(18)
-    q, kc, vc, k_pool, v_pool, bt, ctx = make_case(rng, 2, 4, 2, 8, [0, 5])
+    q, kc, vc, k_pool, v_pool, bt, ctx = make_case(rng, 2, 4, 2, 32, [0, 5])
     out = o.decode_attention(q, k_pool, v_pool, bt, ctx, np.float32(0.5))
-    assert np.array_equal(out[0], np.zeros((4, 8))), "ctx=0 must give zeros"
+    assert np.array_equal(out[0], np.zeros((4, 32))), "ctx=0 must give zeros"
     assert np.all(np.isfinite(out[1]))
 
 
@@ -233,7 +248,7 @@ def pin_page_permutation_invariant(o):
     leaves the output bitwise unchanged."""
     rng = np.random.default_rng(19)
     lens = [35, 16, 1, 64]
-    q, kc, vc, k_pool, v_pool, bt, ctx = make_case(rng, 4, 8, 2, 16, lens, extra_pages=7)
+    q, kc, vc, k_pool, v_pool, bt, ctx = make_case(rng, 4, 8, 2, 64, lens, extra_pages=7)
     out1 = o.decode_attention(q, k_pool, v_pool, bt, ctx, np.float32(0.25))
     perm = rng.permutation(k_pool.shape[0])       # new position of each page
     k2 = np.empty_like(k_pool)
@@ -250,9 +265,9 @@ def pin_tail_and_free_pages_ignored(o):
     NaN, +1e30-like and zero fills give bitwise equal outputs."""
     rng = np.random.default_rng(20)
     lens = [17, 30, 5]
-    kc = [random_bf16(rng, (n, 2, 8)) for n in lens]
-    vc = [random_bf16(rng, (n, 2, 8)) for n in lens]
-    q = random_bf16(rng, (3, 4, 8))
+    kc = [random_bf16(rng, (n, 2, 32)) for n in lens]
+    vc = [random_bf16(rng, (n, 2, 32)) for n in lens]
+    q = random_bf16(rng, (3, 4, 32))
     outs = []
     for fill in (NAN_BF16, np.uint16(0x7149), np.uint16(0xF149), np.uint16(0)):
         r = np.random.default_rng(99)                     # same placement each time
@@ -268,7 +283,7 @@ def pin_power_of_two_scale(o):
     """(q * 2^k, scale * 2^-k) gives the same scores exactly, so the same output."""
     rng = np.random.default_rng(21)
     lens = [40, 9]
-    q, kc, vc, k_pool, v_pool, bt, ctx = make_case(rng, 2, 4, 2, 16, lens, sigma=0.5)
+    q, kc, vc, k_pool, v_pool, bt, ctx = make_case(rng, 2, 4, 2, 32, lens, sigma=0.5)
     out1 = o.decode_attention(q, k_pool, v_pool, bt, ctx, np.float32(0.25))
     q4 = f32_to_bf16_bits(bits_to_f64_ref(q).astype(np.float32) * np.float32(4.0))
     assert np.array_equal(bits_to_f64_ref(q4), 4.0 * bits_to_f64_ref(q))   # exact
@@ -282,7 +297,7 @@ def pin_kv_head_locality(o):
     """Changing the V of KV head j changes exactly q heads [jG, (j+1)G)."""
     rng = np.random.default_rng(22)
     lens = [23]
-    hq, hkv, d = 12, 3, 8
+    hq, hkv, d = 12, 3, 32
     q, kc, vc, k_pool, v_pool, bt, ctx = make_case(rng, 1, hq, hkv, d, lens)
     base = o.decode_attention(q, k_pool, v_pool, bt, ctx, np.float32(0.3))
     g = hq // hkv
@@ -304,7 +319,7 @@ def pin_gather_roundtrip(o):
     """gather_sequence inverts this module's scatter bit for bit."""
     rng = np.random.default_rng(23)
     lens = [1, 16, 33]
-    q, kc, vc, k_pool, v_pool, bt, ctx = make_case(rng, 3, 4, 2, 8, lens)
+    q, kc, vc, k_pool, v_pool, bt, ctx = make_case(rng, 3, 4, 2, 64, lens)
     for b, n in enumerate(lens):
         kg, vg = o.gather_sequence(k_pool, v_pool, bt[b], n)
         assert np.array_equal(kg, bits_to_f64_ref(kc[b])), f"K gather b={b}"
@@ -316,7 +331,7 @@ def pin_append_then_gather(o):
     with the new row at the end, and no other pool bit changes."""
     rng = np.random.default_rng(24)
     lens = [16, 1, 20, 47, 17]              # new token positions 15, 0, 19, 46, 16
-    hkv, d = 2, 8
+    hkv, d = 2, 64
     kc = [random_bf16(rng, (n, hkv, d)) for n in lens]
     vc = [random_bf16(rng, (n, hkv, d)) for n in lens]
     old = [n - 1 for n in lens]
@@ -334,7 +349,7 @@ def pin_append_then_gather(o):
         kg, vg = o.gather_sequence(k2, v2, bt[b], n)
         assert np.array_equal(kg, bits_to_f64_ref(kc[b])), f"append K b={b}"
         assert np.array_equal(vg, bits_to_f64_ref(vc[b])), f"append V b={b}"
-    kd = k2 != k_pool
+    kd = k_by_slot(k2) != k_by_slot(k_pool)
     vd = v2 != v_pool
     written_k = np.zeros_like(kd)
     written_v = np.zeros_like(vd)
@@ -343,7 +358,7 @@ def pin_append_then_gather(o):
         written_v[bt[b][p // PAGE], :, :, p % PAGE] = True
     assert not np.any(kd & ~written_k), "append touched K bits outside the new slots"
     assert not np.any(vd & ~written_v), "append touched V bits outside the new slots"
-    assert np.all(k2[written_k] != NAN_BF16) and np.all(v2[written_v] != NAN_BF16)
+    assert np.all(k_by_slot(k2)[written_k] != NAN_BF16) and np.all(v2[written_v] != NAN_BF16)
     # a negative position skips the sequence
     pos_skip = pos.copy()
     pos_skip[2] = -1
@@ -352,7 +367,7 @@ def pin_append_then_gather(o):
     keep_v = written_v.copy()
     keep_k[bt[2][old[2] // PAGE], :, old[2] % PAGE, :] = False
     keep_v[bt[2][old[2] // PAGE], :, :, old[2] % PAGE] = False
-    assert np.array_equal(k3 != k_pool, keep_k), "skipped sequence: K bits changed"
+    assert np.array_equal(k_by_slot(k3) != k_by_slot(k_pool), keep_k), "skipped sequence: K bits changed"
     assert np.array_equal(v3 != v_pool, keep_v), "skipped sequence: V bits changed"
 
 
@@ -380,8 +395,8 @@ def pin_prefill_sdpa_library(o):
     mask (key j visible to chunk token i iff j <= before + i) otherwise."""
     import torch
     rng = np.random.default_rng(41)
-    for hq, hkv, d, befores, chunks in [(8, 2, 16, [0, 0], [1, 37]),
-                                        (6, 3, 8, [5, 16, 40], [20, 3, 17]),
+    for hq, hkv, d, befores, chunks in [(8, 2, 64, [0, 0], [1, 37]),
+                                        (6, 3, 32, [5, 16, 40], [20, 3, 17]),
                                         (7, 1, 32, [0, 31], [33, 1])]:
         q, kc, vc, k_pool, v_pool, bt, qs, bef, k_rows, v_rows = make_prefill_case(
             rng, hq, hkv, d, befores, chunks)
@@ -409,7 +424,7 @@ def pin_prefill_last_row_is_decode(o):
     decode attention over before + chunk tokens of the written pool."""
     rng = np.random.default_rng(42)
     q, kc, vc, k_pool, v_pool, bt, qs, bef, k_rows, v_rows = make_prefill_case(
-        rng, 8, 4, 16, [0, 9, 32], [5, 30, 1])
+        rng, 8, 4, 32, [0, 9, 32], [5, 30, 1])
     out, k2, v2 = o.prefill_attention(q, k_pool, v_pool, k_rows, v_rows, qs, bt, bef, 0.25)
     last = qs[1:] - 1
     ref = o.decode_attention(q[last], k2, v2, bt, bef + np.diff(qs), 0.25)
@@ -421,7 +436,7 @@ def pin_prefill_causality(o):
     before it keep every bit."""
     rng = np.random.default_rng(43)
     q, kc, vc, k_pool, v_pool, bt, qs, bef, k_rows, v_rows = make_prefill_case(
-        rng, 4, 2, 8, [7], [12])
+        rng, 4, 2, 32, [7], [12])
     base, _, _ = o.prefill_attention(q, k_pool, v_pool, k_rows, v_rows, qs, bt, bef, 0.5)
     for j in (0, 5, 11):
         k2, v2 = k_rows.copy(), v_rows.copy()
@@ -437,7 +452,7 @@ def pin_prefill_write_matches_appends(o):
     for bit; nothing else in the pools changes."""
     rng = np.random.default_rng(44)
     q, kc, vc, k_pool, v_pool, bt, qs, bef, k_rows, v_rows = make_prefill_case(
-        rng, 4, 2, 8, [0, 14, 3], [20, 2, 0])
+        rng, 4, 2, 64, [0, 14, 3], [20, 2, 0])
     k_w, v_w = o.kv_write(k_pool, v_pool, k_rows, v_rows, qs, bt, bef)
     k_a, v_a = k_pool.copy(), v_pool.copy()
     chunks = np.diff(qs)
@@ -451,10 +466,10 @@ def pin_prefill_write_matches_appends(o):
         for i in range(int(chunks[b])):
             pos = int(bef[b]) + i
             page = bt[b][pos // PAGE]
-            assert np.array_equal(k_w[page, :, pos % PAGE, :], k_rows[qs[b] + i])
+            assert np.array_equal(k_by_slot(k_w)[page, :, pos % PAGE, :], k_rows[qs[b] + i])
             assert np.array_equal(v_w[page, :, :, pos % PAGE], v_rows[qs[b] + i])
             written += 1
-    changed = int(np.count_nonzero(np.any(k_w != k_pool, axis=-1)))
+    changed = int(np.count_nonzero(np.any(k_by_slot(k_w) != k_by_slot(k_pool), axis=-1)))
     assert changed <= written * k_pool.shape[1], "bits outside the written slots changed"
 
 
@@ -462,7 +477,7 @@ def pin_prefill_one_token_is_decode(o):
     """A one-token chunk is one append then one decode step."""
     rng = np.random.default_rng(45)
     q, kc, vc, k_pool, v_pool, bt, qs, bef, k_rows, v_rows = make_prefill_case(
-        rng, 6, 2, 16, [0, 1, 16, 47], [1, 1, 1, 1])
+        rng, 6, 2, 32, [0, 1, 16, 47], [1, 1, 1, 1])
     out, k2, v2 = o.prefill_attention(q, k_pool, v_pool, k_rows, v_rows, qs, bt, bef, 0.3)
     k3, v3 = o.kv_append(k_pool, v_pool, k_rows, v_rows, bt, bef.astype(np.int32))
     assert np.array_equal(k2, k3) and np.array_equal(v2, v3)

@@ -26,7 +26,7 @@ def test_serving_loop_over_scheduler_pages():
     scale = 0.125
     rng = np.random.default_rng(2024)
     sched = B.Scheduler(P, L, MB, STRIDE)
-    k_host = np.full((P, HKV, 16, D), NAN, np.uint16)
+    k_host = np.full((P, HKV, D // 32, 16, 32), NAN, np.uint16)
     v_host = np.full((P, HKV, D, 16), NAN, np.uint16)
     k_dev = torch.from_numpy(k_host.view(np.int16).copy()).to(dev)
     v_dev = torch.from_numpy(v_host.view(np.int16).copy()).to(dev)
@@ -106,7 +106,7 @@ def test_chunked_prefill_then_decode_over_scheduler_pages():
     scale = float(np.float32(1.0 / np.sqrt(D)))
     rng = np.random.default_rng(77)
     sched = B.Scheduler(P, L, MB, STRIDE)
-    k_host = np.full((P, HKV, 16, D), NAN, np.uint16)
+    k_host = np.full((P, HKV, D // 32, 16, 32), NAN, np.uint16)
     v_host = np.full((P, HKV, D, 16), NAN, np.uint16)
     k_dev = torch.from_numpy(k_host.view(np.int16).copy()).to(dev)
     v_dev = torch.from_numpy(v_host.view(np.int16).copy()).to(dev)

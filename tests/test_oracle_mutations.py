@@ -32,10 +32,14 @@ MUTATIONS = {
     "bf16_shift": ("(bits.astype(np.uint32) << 16)", "(bits.astype(np.uint32) << 15)"),
     "query_head_kv_row": ("out[b, h] = attend_one_head(qb[h], kc[:, g, :], vc[:, g, :], scale)",
                           "out[b, h] = attend_one_head(qb[g], kc[:, g, :], vc[:, g, :], scale)"),
-    "append_wrong_slot": ("k_out[physical, g, slot, :] = k_new[b, g, :]",
-                          "k_out[physical, g, (slot + 1) % PAGE_SIZE, :] = k_new[b, g, :]"),
-    "append_v_wrong_head": ("v_out[physical, g, :, slot] = v_new[b, g, :]",
-                            "v_out[physical, g, :, slot] = v_new[b, 0, :]"),
+    "append_wrong_slot": ("set_k_slot_row(k_out, physical, slot, k_new[b])",
+                          "set_k_slot_row(k_out, physical, (slot + 1) % PAGE_SIZE, k_new[b])"),
+    "append_v_wrong_head": ("v_out[physical, :, :, slot] = v_new[b]",
+                            "v_out[physical, :, :, slot] = v_new[b, :1]"),
+    "k_read_slabs_transposed": ("return k_pool[physical, :, :, slot, :].reshape(",
+                                "return k_pool[physical, :, :, slot, :].transpose(0, 2, 1).reshape("),
+    "k_write_slabs_reversed": ("k_pool[physical, :, :, slot, :] = rows.reshape(rows.shape[0], -1, K_SLAB)",
+                               "k_pool[physical, :, :, slot, :] = rows.reshape(rows.shape[0], -1, K_SLAB)[:, ::-1]"),
     "append_ignores_skip": ("if pos < 0:\n            continue", "if pos < -10**9:\n            continue"),
     "ctx_zero_not_zero": ("if n == 0:\n            continue\n        kc, vc",
                           "if n == 0:\n            out[b] = 1.0\n            continue\n        kc, vc"),

@@ -80,7 +80,7 @@ def test_poison_marks_exactly_the_empty_slots():
         for t in range(int(n)):
             p, s = pages[t // 16], t % 16
             is_nan = t == n - 1          # the append slot stays empty until written
-            assert np.all((k[p, :, s, :] == W.NAN_BITS) == is_nan)
+            assert np.all((k[p, :, :, s, :] == W.NAN_BITS) == is_nan)
             assert np.all((v[p, :, :, s] == W.NAN_BITS) == is_nan)
     assert w.positions.tolist() == [4, 15, 32]
 
@@ -123,8 +123,8 @@ def test_prefill_workloads(name):
     page = int(w.base.block_tables[0, b, c // W.PAGE])
     kp = w.base.pool_pages_bits("k", [page])[0]
     slots = np.arange(W.PAGE)
-    assert np.all((kp[:, slots >= c % W.PAGE] == W.NAN_BITS))
-    assert not np.any(kp[:, slots < c % W.PAGE] == W.NAN_BITS)
+    assert np.all((kp[:, :, slots >= c % W.PAGE] == W.NAN_BITS))
+    assert not np.any(kp[:, :, slots < c % W.PAGE] == W.NAN_BITS)
     # row generators: host rows equal the device-path rows, layers differ
     rows = np.array([0, 1, w.num_rows - 1])
     small = W.PrefillWorkload(base=w.base, ctx_before=w.ctx_before, chunks=w.chunks)
