@@ -180,6 +180,7 @@ struct PrefillWave {
   int first_pos;          // position of the wave's first token (keys up to it are seen by every row)
   int pos[RG];            // this lane's query position per row group (rows past the chunk: last_pos)
   float sl2;
+  uint32_t neg_lo, neg_hi;  // BF16 pairs (-1, 0) and (0, -1), held opaque (see split_low)
   bf16x8 qf[RG][D / 32];  // the lane's query row per row group, B operand
 };
 
@@ -187,6 +188,23 @@ template <int D, int RG>
 __device__ __forceinline__ int clamp_pid(const PrefillWave<D, RG>& w, int logical) {
   const int p = w.bt_row[logical];
   return p < 0 ? 0 : (p >= w.num_pages ? w.num_pages - 1 : p);
+}
+
+// Maximum over the 4 lanes that hold one row (l, l ^ 16, l ^ 32, l ^ 48),
+// with gfx950's lane-swap instructions instead of LDS permutes: swapping a
+// value with a copy of itself leaves the values of lanes l and l ^ 16 (or
+// l ^ 32) in the two results. The copy is made opaque, so the compiler keeps
+// the two results apart (handed one value twice, it merged them).
+__device__ __forceinline__ float row_max4(float v) {
+  uint32_t a = __float_as_uint(v), b = a;
+  asm volatile("" : "+v"(b));
+  const auto s16 = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  v = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+  a = __float_as_uint(v);
+  b = a;
+  asm volatile("" : "+v"(b));
+  const auto s32 = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  return fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
 }
 
 // How far (log2 units) a row's running max may trail its true max before the
@@ -220,26 +238,30 @@ __device__ __forceinline__ void prefill_compute(const PrefillWave<D, RG>& w, Pre
 #pragma unroll
     for (int e = 0; e < 8; ++e) sv[e] = sc[e >> 2][e & 3];
     if (diag) {
+      const int lim = w.pos[g] - key0;     // key0 + e is visible iff e <= lim
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sv[e] = (key0 + e <= w.pos[g]) ? sv[e] : -INFINITY;
+      for (int e = 0; e < 8; ++e) sv[e] = (e <= lim) ? sv[e] : -INFINITY;
     }
     float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    mx = xor_max(mx, 16);
-    mx = xor_max(mx, 32);
+    mx = row_max4(mx);
     // raw scores times a positive sl2 (the sign of the scale is folded into q)
     const float mx2 = mx * w.sl2;
     const float m_old = st[g].m;
     const float m_new = mx2 > m_old + kLazyMax ? mx2 : m_old;
     const float alpha = __builtin_amdgcn_exp2f(m_old - m_new);
-    float psum = 0.f;
+    float psum;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       const f32x2 pv = {__builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], w.sl2, -m_new)),
                         __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e + 1], w.sl2, -m_new))};
-      psum += pv[0] + pv[1];
+      psum = e == 0 ? pv[0] + pv[1] : psum + (pv[0] + pv[1]);
       const bf16x2 hi = __builtin_convertvector(pv, bf16x2);
-      const bf16x2 lo = __builtin_convertvector(pv - __builtin_convertvector(hi, f32x2), bf16x2);
+      // low halves p - float(hi), exactly: hi . (-1, 0) + p0 and hi . (0, -1) + p1
+      // (BF16 products are exact in FP32 and the sums are representable)
+      const f32x2 low = {__builtin_amdgcn_fdot2_f32_bf16(hi, __builtin_bit_cast(bf16x2, w.neg_lo), pv[0], false),
+                         __builtin_amdgcn_fdot2_f32_bf16(hi, __builtin_bit_cast(bf16x2, w.neg_hi), pv[1], false)};
+      const bf16x2 lo = __builtin_convertvector(low, bf16x2);
       ph[g][e] = hi[0];
       ph[g][e + 1] = hi[1];
       pl[g][e] = lo[0];
@@ -349,6 +371,13 @@ __global__ __launch_bounds__(256, prefill_occupancy<D>()) void prefill_kernel(Pr
   const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
   const bool qzero = a.scale_log2 == 0.f;
   w.sl2 = qzero ? 1.f : fabsf(a.scale_log2);
+  // Held in registers the compiler cannot see into: folded to an inline
+  // constant, the pair (-1, 0) was encoded as FP32 -1.0, which
+  // v_dot2_f32_bf16 reads as the pair (0, -1).
+  w.neg_lo = 0x0000BF80u;
+  w.neg_hi = 0xBF800000u;
+  asm volatile("" : "+s"(w.neg_lo));
+  asm volatile("" : "+s"(w.neg_hi));
   size_t qrow[RG];
   bool valid[RG];
 #pragma unroll
