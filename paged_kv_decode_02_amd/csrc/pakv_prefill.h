@@ -27,8 +27,10 @@
 //     grp = lane / 16) ends up with slots 8 (grp % 2) + 0..7 of page grp / 2
 //     for row r: 8 consecutive keys, positions 32 pair + 8 grp + 0..7;
 //   causal mask by select (only on pairs that cross the diagonal), FP32
-//     online softmax per row (the 4 lanes holding a row reduce their maxima
-//     with two xor shuffles), the running max allowed to trail by 2^8;
+//     online softmax per row: weights against the running max as it stands;
+//     the row maxima (over the 4 lanes holding a row, by lane swaps) are
+//     found only when some lane's weight sum passes 2^8, and the running max
+//     moves only when it trails the row's max by more than 8 (log2 units);
 //   O^T += V^T P^T on the matrix cores: A = V^T (16 head dims x those 8 keys
 //     per lane group: 16 contiguous bytes of a slot-minor V row), B = P^T,
 //     P split into BF16 hi + lo as in decode.
@@ -208,9 +210,11 @@ __device__ __forceinline__ float row_max4(float v) {
 }
 
 // How far (log2 units) a row's running max may trail its true max before the
-// accumulators are rescaled: weights then stay below 2^8, and a rescale
-// happens only when a row's maximum grows by more than that.
+// accumulators are rescaled: weights then stay at most 2^8, and a rescale
+// happens only when a row's maximum grows by more than that. A lane whose
+// weight sum is within kLazyBound has every weight within it.
 constexpr float kLazyMax = 8.f;
+constexpr float kLazyBound = 256.f;   // 2^kLazyMax
 
 template <int D, int RG>
 __device__ __forceinline__ void prefill_compute(const PrefillWave<D, RG>& w, PrefillPair<D>& buf, int pr,
@@ -242,37 +246,55 @@ __device__ __forceinline__ void prefill_compute(const PrefillWave<D, RG>& w, Pre
 #pragma unroll
       for (int e = 0; e < 8; ++e) sv[e] = (e <= lim) ? sv[e] : -INFINITY;
     }
-    float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    mx = row_max4(mx);
-    // raw scores times a positive sl2 (the sign of the scale is folded into q)
-    const float mx2 = mx * w.sl2;
+    // Weights against the running max as it stands. Each is at most the
+    // lane's sum, so while every lane's sum stays within 2^kLazyMax the row
+    // maxima need not be found; otherwise (and on a row's first keys, while
+    // its max is -inf and the sums are not finite) the wave finds them,
+    // moves a max that trails by more than kLazyMax, and recomputes.
     const float m_old = st[g].m;
-    const float m_new = mx2 > m_old + kLazyMax ? mx2 : m_old;
-    const float alpha = __builtin_amdgcn_exp2f(m_old - m_new);
+    f32x2 pv[4];
     float psum;
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const f32x2 pv = {__builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], w.sl2, -m_new)),
-                        __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e + 1], w.sl2, -m_new))};
-      psum = e == 0 ? pv[0] + pv[1] : psum + (pv[0] + pv[1]);
-      const bf16x2 hi = __builtin_convertvector(pv, bf16x2);
-      // low halves p - float(hi), exactly: hi . (-1, 0) + p0 and hi . (0, -1) + p1
-      // (BF16 products are exact in FP32 and the sums are representable)
-      const f32x2 low = {__builtin_amdgcn_fdot2_f32_bf16(hi, __builtin_bit_cast(bf16x2, w.neg_lo), pv[0], false),
-                         __builtin_amdgcn_fdot2_f32_bf16(hi, __builtin_bit_cast(bf16x2, w.neg_hi), pv[1], false)};
-      const bf16x2 lo = __builtin_convertvector(low, bf16x2);
-      ph[g][e] = hi[0];
-      ph[g][e + 1] = hi[1];
-      pl[g][e] = lo[0];
-      pl[g][e + 1] = lo[1];
+    for (int q = 0; q < 4; ++q) {
+      pv[q] = f32x2{__builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * q], w.sl2, -m_old)),
+                    __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * q + 1], w.sl2, -m_old))};
+      psum = q == 0 ? pv[q][0] + pv[q][1] : psum + (pv[q][0] + pv[q][1]);
+    }
+    float alpha = 1.f;
+    if (__ballot(!(psum <= kLazyBound))) {
+      float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      mx = row_max4(mx);
+      // raw scores times a positive sl2 (the sign of the scale is folded into q)
+      const float mx2 = mx * w.sl2;
+      const float m_new = mx2 > m_old + kLazyMax ? mx2 : m_old;
+      alpha = __builtin_amdgcn_exp2f(m_old - m_new);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        pv[q] = f32x2{__builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * q], w.sl2, -m_new)),
+                      __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * q + 1], w.sl2, -m_new))};
+        psum = q == 0 ? pv[q][0] + pv[q][1] : psum + (pv[q][0] + pv[q][1]);
+      }
+      if (__ballot(m_new != m_old)) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) st[g].acc[mt] *= alpha;
+      }
+      st[g].m = m_new;
     }
     st[g].l = st[g].l * alpha + psum;
-    if (__ballot(m_new != m_old)) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) st[g].acc[mt] *= alpha;
+    for (int q = 0; q < 4; ++q) {
+      const bf16x2 hi = __builtin_convertvector(pv[q], bf16x2);
+      // low halves p - float(hi), exactly: hi . (-1, 0) + p0 and hi . (0, -1) + p1
+      // (BF16 products are exact in FP32 and the sums are representable)
+      const f32x2 low = {__builtin_amdgcn_fdot2_f32_bf16(hi, __builtin_bit_cast(bf16x2, w.neg_lo), pv[q][0], false),
+                         __builtin_amdgcn_fdot2_f32_bf16(hi, __builtin_bit_cast(bf16x2, w.neg_hi), pv[q][1], false)};
+      const bf16x2 lo = __builtin_convertvector(low, bf16x2);
+      ph[g][2 * q] = hi[0];
+      ph[g][2 * q + 1] = hi[1];
+      pl[g][2 * q] = lo[0];
+      pl[g][2 * q + 1] = lo[1];
     }
-    st[g].m = m_new;
   }
   // keys past the wave's last position may be unwritten (NaN): zero their V
   // (dword q holds the lane's keys 2q, 2q+1: positions key0 + 2q, key0 + 2q + 1)
