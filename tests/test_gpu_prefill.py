@@ -136,3 +136,50 @@ def test_prefill_any_scale(scale):
     ref, _, _ = oracle.prefill_attention(c.q, c.k_pool, c.v_pool, c.k_rows, c.v_rows, c.qs, c.bt, c.bef,
                                          c.scale)
     check_parity(out, ref, f"prefill scale {scale}")
+
+
+@pytest.mark.parametrize("name", ["prefill", "prefill_d128", "prefill_chunked"])
+def test_prefill_workload_full_size_sampled(name):
+    """The benchmark's prefill workloads at full size, launched as the
+    benchmark launches them (one pa_prefill per layer over the whole batch):
+    on sampled sequences of the first and last layer, the pages after the
+    chunk write equal the oracle's write bit for bit, and sampled chunk rows
+    (always the first and the last) match the oracle computed row by row."""
+    import torch
+    from paged_kv_decode_02_amd import workloads as W
+    dev = device()
+    w = W.make_prefill_workload(name)
+    base = w.base
+    k_dev, v_dev = base.pool_device("k", dev), base.pool_device("v", dev)
+    pool = B.Pool(k_dev, v_dev)
+    bt = torch.from_numpy(np.ascontiguousarray(base.block_tables)).to(dev)
+    qs = torch.from_numpy(w.query_start).to(dev)
+    before = torch.from_numpy(w.ctx_before).to(dev)
+    q, k_rows, v_rows = w.rows_device("q", dev), w.rows_device("k", dev), w.rows_device("v", dev)
+    g = base.num_q_heads // base.num_kv_heads
+    rng = np.random.default_rng(31)
+    for layer in sorted({0, base.num_layers - 1}):
+        log(f"{name}: layer {layer}, {w.num_rows} rows, before={w.ctx_before.tolist()} entry=pa_prefill")
+        out = B.prefill(pool, q[layer], k_rows[layer], v_rows[layer], qs, bt[layer], before,
+                        float(base.scale), int(w.chunks.max())).cpu().numpy()
+        for b in sorted(rng.choice(len(w.chunks), size=min(3, len(w.chunks)), replace=False).tolist()):
+            n_tot = int(w.ctx_before[b]) + int(w.chunks[b])
+            pages = base.block_tables[layer, b, :-(-n_tot // 16)].astype(np.int64)
+            rows = np.arange(w.query_start[b], w.query_start[b + 1])
+            local_bt = np.arange(pages.size, dtype=np.int32)[None, :]
+            kp, vp = oracle.kv_write(base.pool_pages_bits("k", pages), base.pool_pages_bits("v", pages),
+                                     w.rows_bits("k", layer, rows), w.rows_bits("v", layer, rows),
+                                     np.array([0, rows.size]), local_bt, np.array([w.ctx_before[b]]))
+            idx = torch.from_numpy(pages).to(dev)
+            assert np.array_equal(k_dev[idx].cpu().numpy().view(np.uint16), kp), f"{name} K pages, seq {b}"
+            assert np.array_equal(v_dev[idx].cpu().numpy().view(np.uint16), vp), f"{name} V pages, seq {b}"
+            kc, vc = oracle.gather_sequence(kp, vp, local_bt[0], n_tot)
+            pick = sorted({0, rows.size - 1, *rng.integers(0, rows.size, 4).tolist()})
+            qsel = w.rows_bits("q", layer, rows[pick])
+            for j, i in enumerate(pick):
+                p = int(w.ctx_before[b]) + i
+                qr = oracle.bf16_bits_to_f64(qsel[j])
+                ref = np.stack([oracle.attend_one_head(qr[h], kc[:p + 1, h // g], vc[:p + 1, h // g],
+                                                       float(base.scale)) for h in range(base.num_q_heads)])
+                check_parity(out[rows[i]], ref, f"{name} layer {layer} seq {b} row {i}")
+        del out
