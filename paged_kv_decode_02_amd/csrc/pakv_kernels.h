@@ -112,8 +112,8 @@ __device__ __forceinline__ int clamp_ctx(int n, int stride) {
 
 // K/V pages are read once per launch: they are loaded with the nontemporal
 // hint (streaming cache policy), measured faster for d = 64 (K and V) and for
-// the V tiles of d = 128; the d = 128 K loads, whose 16-byte pieces of a
-// 128-byte line come from four instructions, measured slower with it.
+// the V tiles of d = 128; the d = 128 K tiles measured no faster with it
+// (slightly slower), so they keep the default policy.
 template <int D>
 __host__ __device__ constexpr bool nt_k() { return D == 64; }
 template <int D>
@@ -615,8 +615,9 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(DecodeArgs a, int spl
 
 // ---------------------------------------------------------------- append
 // One 256-thread block per sequence: a bit copy of the new token's K row
-// (16-byte chunks) and of its V values into the slot-minor V layout, each V
-// slot row (32 bytes) read, patched and written whole.
+// (16-byte chunks, each to its slab of the K tile) and of its V values into
+// the slot-minor V layout, each V slot row (32 bytes) read, patched and
+// written whole.
 template <int D>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   const int t = threadIdx.x;

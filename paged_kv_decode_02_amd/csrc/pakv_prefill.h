@@ -103,7 +103,7 @@ __device__ __forceinline__ Chunk load_chunk(const int32_t* query_start, const in
 
 // ------------------------------------------------------------ chunk write
 // One 256-thread block per (sequence, page the chunk touches): K rows are
-// 16-byte copies; every V slot row (32 bytes, one head dim of one KV head) of
+// 16-byte copies into their slabs; every V slot row (32 bytes, one head dim of one KV head) of
 // the page is built from the chunk's tokens, reading the old row first only
 // when the chunk covers part of the page.
 template <int D>
