@@ -123,43 +123,65 @@ __global__ __launch_bounds__(256) void kv_write_kernel(WriteArgs a) {
   const int row_of_slot0 = ch.r0 + pg * kPage - ch.c;             // chunk row of slot 0
   const int H = a.num_kv_heads;
   const size_t tile0 = (size_t)pid * H;
-  // K: (slot, kv head, 16-byte chunk)
+  // K: (slot, kv head, 16-byte chunk); four loads in flight per thread
   const int kchunks = (s1 - s0) * H * (D / 8);
-  for (int e = threadIdx.x; e < kchunks; e += 256) {
-    const int part = e % (D / 8);
-    const int g = (e / (D / 8)) % H;
-    const int slot = s0 + e / ((D / 8) * H);
-    const size_t row = (size_t)(row_of_slot0 + slot);
-    *(u32x4*)(a.kpool + (tile0 + g) * kPage * D + k_offset(slot, 8 * part)) =
-        *(const u32x4*)(a.k_rows + (row * H + g) * D + 8 * part);
+  for (int e0 = threadIdx.x; e0 < kchunks; e0 += 4 * 256) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * 256;
+      if (e < kchunks) {
+        const int part = e % (D / 8);
+        const int g = (e / (D / 8)) % H;
+        const size_t row = (size_t)(row_of_slot0 + s0 + e / ((D / 8) * H));
+        v[u] = *(const u32x4*)(a.k_rows + (row * H + g) * D + 8 * part);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * 256;
+      if (e < kchunks) {
+        const int part = e % (D / 8);
+        const int g = (e / (D / 8)) % H;
+        const int slot = s0 + e / ((D / 8) * H);
+        *(u32x4*)(a.kpool + (tile0 + g) * kPage * D + k_offset(slot, 8 * part)) = v[u];
+      }
+    }
   }
-  // V: one slot row per (kv head, head dim)
+  // V: one slot row per (kv head, head dim). The chunk's values of that dim
+  // for the page's slots are loaded together (independent 2-byte loads; a
+  // wave covers 64 consecutive dims, so each load is 128 contiguous bytes),
+  // then packed into the row; slots outside the chunk keep their bits.
   const bool whole = s0 == 0 && s1 == kPage;
   for (int e = threadIdx.x; e < H * D; e += 256) {
     const int g = e / D;
     const int dd = e - g * D;
     u32x4* vrow = (u32x4*)(a.vpool + ((tile0 + g) * D + dd) * kPage);
-    u32x4 h0, h1;
+    uint32_t nv[kPage];
+#pragma unroll
+    for (int slot = 0; slot < kPage; ++slot)
+      nv[slot] = (slot >= s0 && slot < s1)
+                     ? (uint32_t)a.v_rows[((size_t)(row_of_slot0 + slot) * H + g) * D + dd] : 0u;
+    u32x4 h[2];
     if (whole) {
-      h0 = u32x4{0u, 0u, 0u, 0u};
-      h1 = h0;
+      h[0] = u32x4{0u, 0u, 0u, 0u};
+      h[1] = h[0];
     } else {
-      h0 = vrow[0];
-      h1 = vrow[1];
+      h[0] = vrow[0];
+      h[1] = vrow[1];
     }
-    for (int slot = s0; slot < s1; ++slot) {
-      const uint32_t nv = a.v_rows[((size_t)(row_of_slot0 + slot) * H + g) * D + dd];
-      const int w = (slot & 7) >> 1;
-      const uint32_t sh = (slot & 1) * 16;
+    // dword i of half q holds slots 8 q + 2 i (low 16 bits) and 8 q + 2 i + 1
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (i != w) continue;
-        if (slot < 8) h0[i] = (h0[i] & ~(0xFFFFu << sh)) | (nv << sh);
-        else h1[i] = (h1[i] & ~(0xFFFFu << sh)) | (nv << sh);
+        const int sa = 8 * q + 2 * i;
+        const uint32_t lo = (sa >= s0 && sa < s1) ? nv[sa] : (h[q][i] & 0xFFFFu);
+        const uint32_t hi = (sa + 1 >= s0 && sa + 1 < s1) ? nv[sa + 1] : (h[q][i] >> 16);
+        h[q][i] = lo | (hi << 16);
       }
-    }
-    vrow[0] = h0;
-    vrow[1] = h1;
+    vrow[0] = h[0];
+    vrow[1] = h[1];
   }
 }
 
