@@ -261,7 +261,8 @@ const char* pa_status_str(pa_status status);
  * with a pair of HIP events on the same stream. pa_profile_stop waits for
  * those events, returns the summed milliseconds and launch counts per kernel
  * kind (index 0: decode split kernel, 1: split merge kernel, 2: append
- * kernel) in ms[3] / launches[3], and stops recording. Not thread-safe.
+ * kernel, 3: chunk write kernel, 4: prefill attention kernel) in ms[5] /
+ * launches[5], and stops recording. Not thread-safe.
  */
 pa_status pa_profile_start(void);
 pa_status pa_profile_stop(double* ms, int64_t* launches);

@@ -506,17 +506,10 @@ pa_status pa_prefill(const pa_pool* pool, const void* q, const void* k_rows, con
   (void)hipGetLastError();
   {
     LaunchTimer t(4, s);
-#if PAKV_PREFILL_LDS
-    if (pool->head_dim == 64)
-      hipLaunchKernelGGL((pakv::prefill_lds_kernel<64>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((pakv::prefill_lds_kernel<128>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
-#else
     if (pool->head_dim == 64)
       hipLaunchKernelGGL((pakv::prefill_kernel<64>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL((pakv::prefill_kernel<128>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
-#endif
   }
   if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
   return PA_OK;

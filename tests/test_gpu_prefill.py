@@ -1,8 +1,9 @@
 """Paged prefill on the GPU (pa_kv_write, pa_prefill) against the oracle:
 chunk writes bit for bit, causal attention rows within the parity bar, on
-chunks that start and end inside pages, continue an existing cache, or are
-empty; grouped heads G = 1, 4, 7, 16; head_dim 64 and 128; and a 2048-token
-prompt checked on sampled rows."""
+chunks that start and end inside pages, continue an existing cache (up to
+5000 tokens), or are empty; grouped heads G = 1, 2, 4, 7, 8, 16; head_dim 64
+and 128; and long prompts and the benchmark's workloads checked on sampled
+rows."""
 
 import numpy as np
 import pytest
@@ -49,6 +50,11 @@ CASES = [
     ("g8_d128", 8, 1, 128, [15], [49]),
     ("g16_d128", 32, 2, 128, [0, 40], [33, 90]),
     ("g2_d64", 4, 2, 64, [3], [130]),
+    # rows that see more than 2048 keys (caches of up to 5000 tokens)
+    ("long_cache_d64", 32, 8, 64, [3000, 70, 5000], [40, 200, 130]),
+    ("long_cache_d128", 28, 4, 128, [4100, 2000], [33, 150]),
+    ("across_2048_d64", 8, 2, 64, [1990], [300]),
+    ("long_fresh_g8", 8, 1, 64, [0], [2500]),
 ]
 
 
