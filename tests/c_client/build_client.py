@@ -1,0 +1,40 @@
+"""Build step for the plain C client of libpakv (test infrastructure):
+gcc, C11, the HIP runtime's C API and libpakv.so from the package directory.
+
+    python tests/c_client/build_client.py
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+PKG = os.path.join(ROOT, "paged_kv_decode_02_amd")
+SRC = os.path.join(HERE, "pakv_client.c")
+OUT = os.path.join(HERE, "pakv_client")
+
+
+def build() -> str:
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler for the C client")
+    if not os.path.exists(os.path.join(PKG, "libpakv.so")):
+        raise RuntimeError("libpakv.so is not built")
+    cmd = [cc, "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I/opt/rocm/include", f"-I{os.path.join(ROOT, 'include')}", SRC, "-o", OUT + ".tmp",
+           "-L/opt/rocm/lib", "-lamdhip64", f"-L{PKG}", "-l:libpakv.so", "-lm",
+           "-Wl,-rpath,/opt/rocm/lib", "-Wl,-rpath,$ORIGIN/../../paged_kv_decode_02_amd"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"C client build failed:\n{res.stderr}")
+    os.replace(OUT + ".tmp", OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    print(build())
+    sys.exit(0)
