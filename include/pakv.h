@@ -74,7 +74,15 @@
 extern "C" {
 #endif
 
-typedef enum pa_status {
+/* Status codes. Compiled as C++ the enum is given int as its underlying
+ * type, so that any int a C caller passes (pa_status_str of an unknown
+ * code, say) is a valid value on both sides; the size and the calling
+ * convention are those of an int either way. */
+typedef enum pa_status
+#ifdef __cplusplus
+    : int
+#endif
+{
   PA_OK = 0,
   PA_ERR_NULL = 1,        /* a required pointer is NULL */
   PA_ERR_INVALID = 2,     /* a count or size is out of range */

@@ -1,0 +1,177 @@
+/*
+ * abi_fuzz.c - the host-side code of libpakv (pakv.hip compiled for the
+ * host only) under AddressSanitizer and UBSan (tests/test_abi_sanitized.py):
+ *   - pa_decode_plan on random context lengths, block-table widths and head
+ *     dims, into plan buffers of exactly the stated capacity: every existing
+ *     (sequence, split) appears once (an empty context once, as split 0),
+ *     page counts never increase along the plan outside the reversed tiers
+ *     of a one-round grid, and a capacity one short is refused untouched;
+ *   - the sizing calls and pa_status_str over every code and beyond;
+ *   - the argument checks of every entry point that queues work, always with
+ *     an argument they must refuse, so nothing reaches the HIP runtime.
+ * Usage: abi_fuzz <seed> <rounds>. Exit status 0 when every check holds.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "pakv.h"
+
+static uint64_t g_state;
+static uint32_t rnd(uint32_t n) {   /* splitmix64 */
+  uint64_t z = (g_state += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  return n ? (uint32_t)(z % n) : 0u;
+}
+
+static void fail(const char* what, long round) {
+  fprintf(stderr, "abi_fuzz: %s (round %ld)\n", what, round);
+  exit(1);
+}
+
+/* fake device pointers: never dereferenced by the host code */
+#define DEV ((void*)(uintptr_t)0x100000)
+#define DEV_MIS ((void*)(uintptr_t)0x100002)
+
+static void plan_round(long round) {
+  const int d = rnd(2) ? 64 : 128;
+  const int hkv = 1 + (int)rnd(8);
+  pa_pool* pool = NULL;
+  if (pa_pool_create(&pool, DEV, DEV, 1 + (int)rnd(100000), 16, hkv, d) != PA_OK) fail("pool", round);
+  const int32_t num_seqs = (int32_t)rnd(300);
+  const int32_t stride = 1 + (int32_t)rnd(rnd(4) ? 300 : 3000);
+  const int64_t cap = pa_decode_plan_capacity(pool, num_seqs, stride);
+  if (cap < 0) fail("capacity", round);
+  int32_t* ctx = (int32_t*)malloc(sizeof(int32_t) * (size_t)(num_seqs ? num_seqs : 1));
+  if (!ctx) fail("oom", round);
+  for (int b = 0; b < num_seqs; ++b) {
+    const uint32_t k = rnd(10);
+    ctx[b] = k == 0 ? 0 : k == 1 ? -(int32_t)rnd(100) : k == 2 ? stride * 16 + (int32_t)rnd(5000)
+                                                              : (int32_t)rnd((uint32_t)stride * 16 + 1);
+  }
+  const int split_tok = pa_split_tokens(d);
+  if (split_tok <= 0 || split_tok % 32 != 0) fail("split tokens", round);
+  const int sp = split_tok / 16;
+  /* the exact item count */
+  int64_t need = 0;
+  for (int b = 0; b < num_seqs; ++b) {
+    int64_t n = ctx[b] < 0 ? 0 : ctx[b];
+    if (n > (int64_t)stride * 16) n = (int64_t)stride * 16;
+    const int64_t pages = (n + 15) / 16;
+    need += pages == 0 ? 1 : (pages + sp - 1) / sp;
+  }
+  if (need > cap) fail("need above capacity", round);
+  int32_t* plan = (int32_t*)malloc(sizeof(int32_t) * (size_t)(need ? need : 1));
+  if (!plan) fail("oom", round);
+  int32_t items = -1;
+  if (num_seqs > 0 && need > 0) {
+    /* one short: refused, nothing written past the buffer (ASan watches) */
+    if (pa_decode_plan(pool, ctx, num_seqs, stride, plan, need - 1, &items) == PA_OK) fail("short capacity", round);
+  }
+  if (pa_decode_plan(pool, ctx, num_seqs, stride, plan, need, &items) != PA_OK) fail("plan", round);
+  if (items != (num_seqs ? need : 0)) fail("item count", round);
+  /* every (sequence, split) once */
+  char* seen = (char*)calloc((size_t)(num_seqs ? num_seqs : 1) * 2048, 1);
+  if (!seen) fail("oom", round);
+  int64_t prev_pages = INT64_MAX;
+  int order_breaks = 0;
+  for (int32_t i = 0; i < items; ++i) {
+    const uint32_t it = (uint32_t)plan[i];
+    const int b = (int)(it & 0xFFFFFu);
+    const int s = (int)(it >> 20);
+    if (b >= num_seqs || s >= 2048) fail("item out of range", round);
+    if (seen[(size_t)b * 2048 + s]++) fail("item twice", round);
+    int64_t n = ctx[b] < 0 ? 0 : ctx[b];
+    if (n > (int64_t)stride * 16) n = (int64_t)stride * 16;
+    const int64_t pages = (n + 15) / 16;
+    const int64_t ns = pages == 0 ? 1 : (pages + sp - 1) / sp;
+    if (s >= ns) fail("split past the context", round);
+    const int64_t pg = pages == 0 ? 0 : (pages - (int64_t)s * sp < sp ? pages - (int64_t)s * sp : sp);
+    if (pg > prev_pages) ++order_breaks;
+    prev_pages = pg;
+  }
+  /* order: largest first, except for the reversed tiers of a one-round grid
+     (256 CUs x 4 decode workgroups per CU at d = 64, 2 at d = 128) */
+  if (order_breaks > 0 && (int64_t)items * hkv > 256 * (d == 64 ? 4 : 2)) fail("plan order", round);
+  free(seen);
+  free(plan);
+  free(ctx);
+  pa_pool_destroy(pool);
+}
+
+static void validation_round(long round) {
+  pa_pool* pool = NULL;
+  const int d = rnd(2) ? 64 : 128;
+  if (pa_pool_create(&pool, DEV, DEV, 64, 16, 8, d) != PA_OK) fail("pool", round);
+  float* out = (float*)DEV;
+  /* each call carries one argument the host checks refuse */
+  switch (rnd(12)) {
+    case 0:
+      if (pa_decode(pool, DEV, 4, 30, DEV, 4, DEV, 0.1f, out, NULL, 0, NULL) != PA_ERR_INVALID) fail("decode heads", round);
+      break;
+    case 1:
+      if (pa_decode(pool, DEV_MIS, 4, 32, DEV, 4, DEV, 0.1f, out, NULL, 0, NULL) != PA_ERR_ALIGN) fail("decode align", round);
+      break;
+    case 2:
+      if (pa_decode(pool, DEV, 4, 32, DEV, 200, DEV, 0.1f, out, NULL, 0, NULL) != PA_ERR_WORKSPACE) fail("decode workspace", round);
+      break;
+    case 3:
+      if (pa_decode(pool, DEV, 4, 32, DEV, 4, DEV, INFINITY, out, NULL, 0, NULL) != PA_ERR_INVALID) fail("decode scale", round);
+      break;
+    case 4:
+      if (pa_decode_planned(pool, DEV, 4, 32, DEV, 4, DEV, 0.1f, out, NULL, 0, NULL, 1, NULL) != PA_ERR_NULL) fail("planned", round);
+      break;
+    case 5:
+      if (pa_decode_planned(pool, DEV, 4, 32, DEV, 4, DEV, 0.1f, out, NULL, 0, DEV, -1, NULL) != PA_ERR_INVALID) fail("planned items", round);
+      break;
+    case 6:
+      if (pa_decode_append(pool, DEV, NULL, DEV, DEV, 4, 32, DEV, 4, DEV, 0.1f, out, NULL, 0, NULL) != PA_ERR_NULL) fail("append", round);
+      break;
+    case 7:
+      if (pa_kv_append(pool, DEV_MIS, DEV, 4, DEV, 4, DEV, NULL) != PA_ERR_ALIGN) fail("kv_append", round);
+      break;
+    case 8:
+      if (pa_kv_write(pool, DEV, DEV, 4, 10, 8, DEV, DEV, 0, DEV, NULL) != PA_ERR_INVALID) fail("kv_write", round);
+      break;
+    case 9:
+      if (pa_prefill(pool, DEV, DEV, DEV, 2, 8 * 17, 10, 8, DEV, DEV, 4, DEV, 0.1f, out, NULL) != PA_ERR_UNSUPPORTED) fail("prefill group", round);
+      break;
+    case 10:
+      if (pa_prefill(pool, NULL, DEV, DEV, 2, 32, 10, 8, DEV, DEV, 4, DEV, 0.1f, out, NULL) != PA_ERR_NULL) fail("prefill null", round);
+      break;
+    default: {
+      pa_pool* other = NULL;
+      if (pa_pool_create(&other, DEV, DEV, 64, 16, 8, 96) != PA_ERR_UNSUPPORTED) fail("head dim", round);
+      if (other) pa_pool_destroy(other);
+      break;
+    }
+  }
+  if (pa_decode_workspace_bytes(pool, (int32_t)rnd(1000), 32, 1 + (int32_t)rnd(5000)) > ((size_t)1 << 40)) fail("workspace size", round);
+  pa_pool_destroy(pool);
+}
+
+int main(int argc, char** argv) {
+  if (argc != 3) {
+    fprintf(stderr, "usage: abi_fuzz <seed> <rounds>\n");
+    return 2;
+  }
+  g_state = strtoull(argv[1], NULL, 10);
+  const long rounds = strtol(argv[2], NULL, 10);
+  for (int st = -3; st < 20; ++st) {
+    const char* t = pa_status_str((pa_status)st);
+    if (!t || !t[0]) fail("status text", -1);
+  }
+  if (pa_decode_plan_capacity(NULL, 1, 1) >= 0) fail("capacity NULL", -1);
+  int32_t items = 0;
+  if (pa_decode_plan(NULL, NULL, 0, 1, NULL, 0, &items) != PA_ERR_NULL) fail("plan NULL", -1);
+  for (long r = 0; r < rounds; ++r) {
+    plan_round(r);
+    validation_round(r);
+  }
+  printf("abi_fuzz: %ld rounds: ok\n", rounds);
+  return 0;
+}
