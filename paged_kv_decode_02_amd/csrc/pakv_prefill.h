@@ -355,7 +355,15 @@ template <int D>
 __host__ __device__ constexpr int prefill_block_rows() { return 64 * prefill_row_groups<D>(); }
 
 // Grid: KV head fastest, then sequence, then row block from the last one
-// down, so the blocks that see the most keys start first. Wave w of a block
+// down, so the blocks that see the most keys start first. Within each row
+// block the sequences are rotated by rbp + rbp / 4 (rbp: the block's rank
+// from the last): the workgroups reach the 8 XCDs round-robin and then a CU
+// of their XCD in order, so in a grid the device holds at once a CU takes
+// positions t, t + 32, t + 64, ... of its XCD's sequence; without the
+// rotation, whenever the sequence count divides 32 those are row blocks of
+// one sequence, and the CU that draws the longest cache does its four
+// longest blocks while others idle. With it, a CU's four blocks belong to
+// four sequences (8 sequences: offsets 0, 5, 2, 7). Wave w of a block
 // takes rows w * 32 .. w * 32 + 31 in two groups of 16. The 4 waves share
 // every K/V tile: per page pair the workgroup loads K and V once (16-byte
 // loads, each thread its share), stores them to LDS in matrix-core operand
@@ -390,8 +398,9 @@ __global__ __launch_bounds__(256, prefill_occupancy<D>()) void prefill_kernel(Pr
   const int grp = lane >> 4;
   const int kvh = blockIdx.x % a.num_kv_heads;
   const int rest = blockIdx.x / a.num_kv_heads;
-  const int b = rest % a.num_seqs;
-  const int rb = a.row_blocks - 1 - rest / a.num_seqs;
+  const int rbp = rest / a.num_seqs;
+  const int b = (rest % a.num_seqs + rbp + rbp / 4) % a.num_seqs;
+  const int rb = a.row_blocks - 1 - rbp;
   const int G = a.group;
   const Chunk ch = load_chunk(a.query_start, a.ctx_before, b, a.num_rows, a.max_chunk, a.stride);
   const int rows = ch.n * G;
