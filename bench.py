@@ -60,8 +60,8 @@ def counted_traffic(workload, profile=PROFILE, profiled_workload="c4", sources=K
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c4",
                     choices=["tiny", "c2", "c3", "c4", "c5", "prefill", "prefill_d128", "prefill_chunked"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -164,6 +164,25 @@ def capture_step(w, x, B, stream):
     x.graph, x.graph_items = g, plan.numel()
 
 
+def step_percentiles(run_one, steps, stream):
+    """A pass of its own after the timed region: each of `steps` steps
+    bracketed alone by a pair of HIP events on the launch stream. Returns the
+    10th, 50th and 90th percentile of the step time in us."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    with torch.cuda.stream(stream):
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            run_one(i)
+            b.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    return {"p10": round(float(np.percentile(t, 10)), 1), "p50": round(float(np.percentile(t, 50)), 1),
+            "p90": round(float(np.percentile(t, 90)), 1),
+            "note": "each step timed alone by HIP events in a separate pass"}
+
+
 def stream_ceiling(B, dev, stream):
     """Achievable HBM read bandwidth: pa_stream_read over a 4 GiB buffer, each
     of 10 runs timed alone; returns (best, median) GB/s. Run-to-run spread is
@@ -254,14 +273,45 @@ class PrefillInputs:
         self.out = torch.empty((base.num_layers, w.num_rows, base.num_q_heads, base.head_dim),
                                dtype=torch.float32, device=dev)
         self.max_chunk = int(w.chunks.max())
+        # launch plan: made on the host from the host copies of the cache and
+        # chunk lengths once per step (every layer shares it), as for decode
+        self.before_host = w.ctx_before.copy()
+        self.chunks_host = w.chunks.copy()
+        self.stride = int(base.block_tables.shape[2])
+        cap = B.prefill_plan_capacity(self.pool, len(w.chunks), base.num_q_heads, self.max_chunk)
+        self.plan_pin = [torch.empty(max(cap, 1), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self.plan_copied = [None, None]
+        self.plan_dev = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+        self.step_no = 0
+
+
+def upload_prefill_plan(w, x, B, stream):
+    """The prefill launch plan for this step's lengths, made on the host into a
+    pinned buffer and copied to the device on the launch stream."""
+    import torch
+    k = x.step_no & 1
+    x.step_no += 1
+    if x.plan_copied[k] is not None:
+        x.plan_copied[k].synchronize()
+    n = B.prefill_plan_into(x.pool, x.before_host, x.chunks_host, w.base.num_q_heads, x.stride,
+                            x.max_chunk, x.plan_pin[k])
+    plan = x.plan_dev[:n]
+    with torch.cuda.stream(stream):
+        plan.copy_(x.plan_pin[k][:n], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        x.plan_copied[k] = ev
+    return plan
 
 
 def run_prefill_step(w, x, B, stream):
-    """One step: per layer, pa_prefill (the chunk's K/V written into the pages,
-    then causal attention for every chunk token)."""
+    """One step: the launch plan, then per layer pa_prefill_planned (the
+    chunk's K/V written into the pages, then causal attention for every chunk
+    token, row blocks in the plan's order; bit-identical to pa_prefill)."""
+    plan = upload_prefill_plan(w, x, B, stream)
     for layer in range(w.base.num_layers):
-        B.prefill(x.pool, x.q[layer], x.k_rows[layer], x.v_rows[layer], x.qs, x.bt[layer], x.before,
-                  float(w.base.scale), x.max_chunk, out=x.out[layer], stream=stream)
+        B.prefill_planned(x.pool, x.q[layer], x.k_rows[layer], x.v_rows[layer], x.qs, x.bt[layer], x.before,
+                          float(w.base.scale), x.max_chunk, plan, out=x.out[layer], stream=stream)
 
 
 def prefill_cpu_baseline(w, budget_s):
@@ -344,6 +394,7 @@ def prefill_main(args):
     ms_step = e0.elapsed_time(e1) / args.steps
     flops_step = w.flops_per_layer() * base.num_layers
     value = flops_step / (ms_step * 1e-3) / 1e12
+    pct = step_percentiles(lambda i: run_prefill_step(w, x, B, stream), args.steps, stream)
 
     B.profile_start()
     with torch.cuda.stream(stream):
@@ -371,6 +422,7 @@ def prefill_main(args):
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "us_per_step": round(ms_step * 1e3, 1),
+        "us_per_step_percentiles": pct,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -386,6 +438,7 @@ def prefill_main(args):
             "chunk_rows": w.num_rows,
             "cache_before_mean": round(float(w.ctx_before.mean()), 1),
             "flops_per_step": flops_step,
+            "entry": "pa_prefill_planned per layer (plan made on the host each step)",
             "parallelism": "single GPU",
         },
         "roofline": {
@@ -470,6 +523,7 @@ def main():
     ms_step = ms_total / args.steps
     kv_step = w.kv_bytes_per_step()
     value = kv_step / (ms_step * 1e-3) / 1e9
+    pct = step_percentiles(lambda i: run_step(w, xs[i % replicas], B, stream), args.steps, stream)
 
     # Kernel durations: the same K steps again with every kernel the library
     # queues bracketed by HIP events on the launch stream (the brackets add
@@ -510,6 +564,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "us_per_step": round(ms_step * 1e3, 1),
+        "us_per_step_percentiles": pct,
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "higher_is_better": True,
         "scaling": "weak",

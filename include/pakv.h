@@ -259,6 +259,46 @@ pa_status pa_prefill(const pa_pool* pool, const void* q, const void* k_rows, con
                      int32_t max_pages_per_seq, const int32_t* context_lens, float scale,
                      float* out, void* stream);
 
+/*
+ * Launch plan for pa_prefill (optional; the same results bit for bit).
+ * pa_prefill's grid visits every (sequence, row block of 128 query rows) in
+ * a fixed order; the attention of a row block costs in proportion to the
+ * keys its last row can see, which depends on the cache and chunk lengths
+ * the device holds. A host that knows those lengths (the scheduler does)
+ * can order the row blocks by that cost instead, largest first, leaving out
+ * the blocks past each chunk's end: when the whole grid fits the device at
+ * once (row blocks x num_kv_heads <= 256 CUs x the prefill workgroups a CU
+ * holds: 4 at head_dim 64, 1 at 128), every other tier of row blocks that
+ * the CUs of one XCD take in turn is reversed, pairing large blocks with
+ * small ones on each CU, as pa_decode_plan does for splits.
+ *
+ * pa_prefill_plan_capacity: items a plan may need (num_seqs x row blocks
+ * per sequence), or -1 when the sizes are out of range (num_seqs above
+ * 2^20, more than 2^11 row blocks, or a query-head count pa_prefill
+ * refuses).
+ * pa_prefill_plan: writes the plan for the host arrays context_lens_host and
+ * chunk_lens_host ([num_seqs]; the tokens cached before the chunk and the
+ * chunk's length, clamped as the kernels clamp them) into plan[capacity]
+ * (host memory) and its length into *num_items. Item encoding:
+ * b | (row_block << 20). Pure host code; queues nothing.
+ * pa_prefill_planned: pa_prefill's arguments plus plan (device memory, int32
+ * [num_items], a copy of what pa_prefill_plan wrote) and num_items. Items
+ * naming a sequence or row block out of range are skipped on the device; a
+ * plan made from other lengths leaves the rows it misses unwritten.
+ */
+int64_t pa_prefill_plan_capacity(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_chunk);
+pa_status pa_prefill_plan(const pa_pool* pool, const int32_t* context_lens_host,
+                          const int32_t* chunk_lens_host, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t max_pages_per_seq, int32_t max_chunk, int32_t* plan,
+                          int64_t capacity, int32_t* num_items);
+pa_status pa_prefill_planned(const pa_pool* pool, const void* q, const void* k_rows,
+                             const void* v_rows, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_rows, int32_t max_chunk, const int32_t* query_start,
+                             const int32_t* block_tables, int32_t max_pages_per_seq,
+                             const int32_t* context_lens, float scale, float* out,
+                             const int32_t* plan, int32_t num_items, void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* pa_status_str(pa_status status);
 

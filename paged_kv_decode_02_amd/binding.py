@@ -29,7 +29,8 @@ EXPORTS = ["pa_pool_create", "pa_pool_destroy", "pa_kv_append", "pa_decode_works
            "pa_decode_planned", "pa_sched_create", "pa_sched_destroy", "pa_sched_submit",
            "pa_sched_submit_shared", "pa_sched_admit", "pa_sched_slot", "pa_sched_advance",
            "pa_sched_finish", "pa_sched_block_tables", "pa_sched_context_lens", "pa_sched_stats",
-           "pa_kv_write", "pa_prefill"]
+           "pa_kv_write", "pa_prefill", "pa_prefill_plan_capacity", "pa_prefill_plan",
+           "pa_prefill_planned"]
 
 _lib = None
 
@@ -116,6 +117,15 @@ def lib() -> ctypes.CDLL:
                              c.c_int32, c.c_int32, c.c_void_p, c.c_void_p, c.c_int32, c.c_void_p,
                              c.c_float, c.c_void_p, c.c_void_p]
     L.pa_prefill.restype = c.c_int
+    L.pa_prefill_plan_capacity.argtypes = [c.c_void_p, c.c_int32, c.c_int32, c.c_int32]
+    L.pa_prefill_plan_capacity.restype = c.c_int64
+    L.pa_prefill_plan.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_int32, c.c_int32, c.c_int32,
+                                  c.c_int32, c.c_void_p, c.c_int64, c.POINTER(c.c_int32)]
+    L.pa_prefill_plan.restype = c.c_int
+    L.pa_prefill_planned.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_int32, c.c_int32,
+                                     c.c_int32, c.c_int32, c.c_void_p, c.c_void_p, c.c_int32, c.c_void_p,
+                                     c.c_float, c.c_void_p, c.c_void_p, c.c_int32, c.c_void_p]
+    L.pa_prefill_planned.restype = c.c_int
     _lib = L
     return L
 
@@ -339,6 +349,81 @@ def prefill(pool: Pool, q, k_rows, v_rows, query_start, block_tables, context_le
                             num_rows, max_chunk, _ptr(query_start), _ptr(block_tables), stride,
                             _ptr(context_lens), float(scale), _ptr(out), _stream(stream)),
            "pa_prefill")
+    return out
+
+
+def prefill_plan_capacity(pool: Pool, num_seqs: int, num_q_heads: int, max_chunk: int) -> int:
+    cap = int(lib().pa_prefill_plan_capacity(pool.handle, int(num_seqs), int(num_q_heads), int(max_chunk)))
+    if cap < 0:
+        raise PakvError(PA_ERR_INVALID, "pa_prefill_plan_capacity")
+    return cap
+
+
+def _host_i32(a, name):
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    if a.ndim != 1:
+        raise ValueError(f"{name} must be 1-D")
+    return a
+
+
+def prefill_plan_into(pool: Pool, context_lens_host, chunk_lens_host, num_q_heads: int,
+                      max_pages_per_seq: int, max_chunk: int, out) -> int:
+    """Write the prefill launch plan for these host lengths into ``out`` (host
+    int32 memory of at least prefill_plan_capacity items: a numpy array or a CPU
+    torch tensor, e.g. pinned); returns the number of items (pa_prefill_plan)."""
+    import numpy as np
+    ctx = _host_i32(context_lens_host, "context_lens_host")
+    chunks = _host_i32(chunk_lens_host, "chunk_lens_host")
+    if chunks.size != ctx.size:
+        raise ValueError("context_lens_host and chunk_lens_host differ in length")
+    if isinstance(out, np.ndarray):
+        if out.dtype != np.int32 or not out.flags.c_contiguous:
+            raise ValueError("out must be a contiguous int32 array")
+        addr, size = out.ctypes.data, out.size
+    else:
+        import torch
+        if out.dtype != torch.int32 or out.is_cuda or not out.is_contiguous():
+            raise ValueError("out must be a contiguous host int32 tensor")
+        addr, size = out.data_ptr(), out.numel()
+    n = ctypes.c_int32(0)
+    _check(lib().pa_prefill_plan(pool.handle, ctx.ctypes.data, chunks.ctypes.data, ctx.size,
+                                 int(num_q_heads), int(max_pages_per_seq), int(max_chunk), addr, size,
+                                 ctypes.byref(n)), "pa_prefill_plan")
+    return n.value
+
+
+def prefill_plan(pool: Pool, context_lens_host, chunk_lens_host, num_q_heads: int, max_pages_per_seq: int,
+                 max_chunk: int):
+    """Host-side prefill launch plan (pa_prefill_plan): an int32 numpy array of
+    items ``b | row_block << 20``, the costliest row block first."""
+    import numpy as np
+    num_seqs = np.asarray(context_lens_host).size
+    cap = prefill_plan_capacity(pool, num_seqs, num_q_heads, max_chunk)
+    plan = np.zeros(max(cap, 1), dtype=np.int32)
+    n = prefill_plan_into(pool, context_lens_host, chunk_lens_host, num_q_heads, max_pages_per_seq,
+                          max_chunk, plan)
+    return plan[:n].copy()
+
+
+def prefill_planned(pool: Pool, q, k_rows, v_rows, query_start, block_tables, context_lens, scale: float,
+                    max_chunk: int, plan, out=None, stream=None):
+    """pa_prefill driven by a launch plan (pa_prefill_planned); ``plan`` is a
+    device int32 tensor holding what prefill_plan returned for the same lengths."""
+    import torch
+    _need(q, "q", _bf16_types(), 3)
+    _need(k_rows, "k_rows", _bf16_types(), 3)
+    _need(v_rows, "v_rows", _bf16_types(), 3)
+    _need(plan, "plan", (torch.int32,), 1)
+    num_seqs, num_rows, stride, max_chunk = _chunk_common(q, query_start, block_tables, context_lens,
+                                                          max_chunk)
+    if out is None:
+        out = torch.empty(tuple(q.shape), dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,), 3)
+    _check(lib().pa_prefill_planned(pool.handle, _ptr(q), _ptr(k_rows), _ptr(v_rows), num_seqs, q.shape[1],
+                                    num_rows, max_chunk, _ptr(query_start), _ptr(block_tables), stride,
+                                    _ptr(context_lens), float(scale), _ptr(out), _ptr(plan), plan.numel(),
+                                    _stream(stream)), "pa_prefill_planned")
     return out
 
 

@@ -53,6 +53,11 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 int split_pages(int d) { return d == 64 ? PAKV_SPLIT_PAGES_D64 : PAKV_SPLIT_PAGES_D128; }
 
+// prefill workgroups (4 waves) one CU holds at once
+int prefill_wgs_per_cu(int d) {
+  return d == 64 ? pakv::prefill_occupancy<64>() : pakv::prefill_occupancy<128>();
+}
+
 // decode workgroups one CU holds at once (waves per SIMD x 4 SIMDs / waves per workgroup)
 int decode_wgs_per_cu(int d) {
   return pakv::occupancy(d) * 4 / (d == 64 ? PAKV_WAVES_D64 : PAKV_WAVES_D128);
@@ -463,11 +468,17 @@ pa_status pa_kv_write(const pa_pool* pool, const void* k_rows, const void* v_row
                       max_pages_per_seq, context_lens, static_cast<hipStream_t>(stream));
 }
 
-pa_status pa_prefill(const pa_pool* pool, const void* q, const void* k_rows, const void* v_rows,
-                     int32_t num_seqs, int32_t num_q_heads, int32_t num_rows, int32_t max_chunk,
-                     const int32_t* query_start, const int32_t* block_tables,
-                     int32_t max_pages_per_seq, const int32_t* context_lens, float scale,
-                     float* out, void* stream) {
+// Row blocks per (sequence, KV head) for chunks of up to max_chunk tokens.
+static int64_t prefill_row_blocks(int d, int64_t max_chunk, int group) {
+  const int block_rows = d == 64 ? pakv::prefill_block_rows<64>() : pakv::prefill_block_rows<128>();
+  return (max_chunk * group + block_rows - 1) / block_rows;
+}
+
+static pa_status prefill_impl(const pa_pool* pool, const void* q, const void* k_rows, const void* v_rows,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_rows, int32_t max_chunk,
+                              const int32_t* query_start, const int32_t* block_tables,
+                              int32_t max_pages_per_seq, const int32_t* context_lens, float scale,
+                              float* out, const int32_t* plan, int32_t plan_items, void* stream) {
   pa_status st = check_chunk_args(pool, num_seqs, num_rows, max_chunk, query_start, block_tables,
                                   max_pages_per_seq, context_lens);
   if (st != PA_OK) return st;
@@ -478,10 +489,20 @@ pa_status pa_prefill(const pa_pool* pool, const void* q, const void* k_rows, con
   if (num_seqs == 0 || num_rows == 0 || max_chunk == 0) return PA_OK;
   if (!q || !k_rows || !v_rows || !out) return PA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_rows) || !aligned16(v_rows) || !aligned16(out)) return PA_ERR_ALIGN;
+  const int64_t row_blocks = prefill_row_blocks(pool->head_dim, max_chunk, group);
+  if (plan) {
+    if (num_seqs > kPlanMaxSeqs || row_blocks > kPlanMaxSplits) return PA_ERR_INVALID;
+    if (!aligned4(plan)) return PA_ERR_ALIGN;
+  }
+  if (plan_items < 0 || plan_items > static_cast<int64_t>(num_seqs) * row_blocks) return PA_ERR_INVALID;
+  if (plan_items > 0 && !plan) return PA_ERR_NULL;
+  const int64_t units = plan ? plan_items : static_cast<int64_t>(num_seqs) * row_blocks;
+  const int64_t blocks = static_cast<int64_t>(pool->num_kv_heads) * units;
+  if (blocks > INT_MAX || row_blocks > INT_MAX) return PA_ERR_INVALID;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = launch_write(pool, k_rows, v_rows, num_seqs, num_rows, max_chunk, query_start, block_tables,
                     max_pages_per_seq, context_lens, s);
-  if (st != PA_OK) return st;
+  if (st != PA_OK || blocks == 0) return st;
   pakv::PrefillArgs a;
   a.kpool = static_cast<const uint16_t*>(pool->k);
   a.vpool = static_cast<const uint16_t*>(pool->v);
@@ -498,11 +519,9 @@ pa_status pa_prefill(const pa_pool* pool, const void* q, const void* k_rows, con
   a.group = group;
   a.stride = max_pages_per_seq;
   a.max_chunk = max_chunk;
-  const int block_rows = pool->head_dim == 64 ? pakv::prefill_block_rows<64>() : pakv::prefill_block_rows<128>();
-  a.row_blocks = static_cast<int32_t>((static_cast<int64_t>(max_chunk) * group + block_rows - 1) / block_rows);
+  a.row_blocks = static_cast<int32_t>(row_blocks);
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-  const int64_t blocks = static_cast<int64_t>(pool->num_kv_heads) * num_seqs * a.row_blocks;
-  if (blocks > INT_MAX) return PA_ERR_INVALID;
+  a.plan = plan;
   (void)hipGetLastError();
   {
     LaunchTimer t(4, s);
@@ -513,6 +532,93 @@ pa_status pa_prefill(const pa_pool* pool, const void* q, const void* k_rows, con
   }
   if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
   return PA_OK;
+}
+
+pa_status pa_prefill(const pa_pool* pool, const void* q, const void* k_rows, const void* v_rows,
+                     int32_t num_seqs, int32_t num_q_heads, int32_t num_rows, int32_t max_chunk,
+                     const int32_t* query_start, const int32_t* block_tables,
+                     int32_t max_pages_per_seq, const int32_t* context_lens, float scale,
+                     float* out, void* stream) {
+  return prefill_impl(pool, q, k_rows, v_rows, num_seqs, num_q_heads, num_rows, max_chunk, query_start,
+                      block_tables, max_pages_per_seq, context_lens, scale, out, nullptr, 0, stream);
+}
+
+int64_t pa_prefill_plan_capacity(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_chunk) {
+  if (!pool || num_seqs < 0 || num_q_heads < 1 || max_chunk < 0) return -1;
+  if (num_q_heads % pool->num_kv_heads != 0) return -1;
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (group > kMaxGroup) return -1;
+  const int64_t row_blocks = prefill_row_blocks(pool->head_dim, max_chunk, group);
+  if (num_seqs > kPlanMaxSeqs || row_blocks > kPlanMaxSplits) return -1;
+  return static_cast<int64_t>(num_seqs) * row_blocks;
+}
+
+pa_status pa_prefill_plan(const pa_pool* pool, const int32_t* context_lens_host,
+                          const int32_t* chunk_lens_host, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t max_pages_per_seq, int32_t max_chunk, int32_t* plan,
+                          int64_t capacity, int32_t* num_items) {
+  if (!pool || !num_items) return PA_ERR_NULL;
+  *num_items = 0;
+  if (max_pages_per_seq < 1) return PA_ERR_INVALID;
+  if (static_cast<int64_t>(max_pages_per_seq) * pakv::kPage > INT_MAX) return PA_ERR_INVALID;
+  if (pa_prefill_plan_capacity(pool, num_seqs, num_q_heads, max_chunk) < 0) return PA_ERR_INVALID;
+  if (num_seqs == 0 || max_chunk == 0) return PA_OK;
+  if (!context_lens_host || !chunk_lens_host || !plan) return PA_ERR_NULL;
+  const int d = pool->head_dim;
+  const int group = num_q_heads / pool->num_kv_heads;
+  const int block_rows = d == 64 ? pakv::prefill_block_rows<64>() : pakv::prefill_block_rows<128>();
+  const int64_t row_blocks = prefill_row_blocks(d, max_chunk, group);
+  const int64_t max_tok = static_cast<int64_t>(max_pages_per_seq) * pakv::kPage;
+  // every row block that holds rows, with the page pairs its rows can see
+  // (the kernel's own clamping of the cache and chunk lengths), visited from
+  // the last row block down and in sequence order, as the unplanned grid
+  struct Item {
+    int64_t pairs;
+    uint32_t code;
+  };
+  std::vector<Item> items;
+  for (int64_t rb = row_blocks - 1; rb >= 0; --rb) {
+    for (int32_t b = 0; b < num_seqs; ++b) {
+      const int64_t c = std::min<int64_t>(std::max(context_lens_host[b], 0), max_tok);
+      int64_t n = std::min<int64_t>(std::max(chunk_lens_host[b], 0), max_chunk);
+      n = std::min(n, max_tok - c);
+      const int64_t rows = n * group;
+      if (rb * block_rows >= rows) continue;
+      const int64_t last_pos = c + std::min<int64_t>(rb * block_rows + block_rows - 1, rows - 1) / group;
+      const int64_t pages = (last_pos + pakv::kPage) / pakv::kPage;
+      items.push_back({(pages + 1) / 2, static_cast<uint32_t>(b) | (static_cast<uint32_t>(rb) << 20)});
+    }
+  }
+  if (static_cast<int64_t>(items.size()) > capacity) return PA_ERR_INVALID;
+  std::stable_sort(items.begin(), items.end(), [](const Item& x, const Item& y) { return x.pairs > y.pairs; });
+  const int64_t total = static_cast<int64_t>(items.size());
+  for (int64_t i = 0; i < total; ++i) plan[i] = static_cast<int32_t>(items[i].code);
+  // A grid the device holds at once: each CU takes the items of one tier
+  // position of its XCD (XCD round-robin over workgroups, KV head fastest,
+  // then the XCD's CUs in order); reversing every other tier pairs the large
+  // items with small ones on each CU.
+  const int hkv = pool->num_kv_heads;
+  const int64_t resident = static_cast<int64_t>(kDeviceCUs) * prefill_wgs_per_cu(d);
+  const int64_t tier = (hkv <= 8 && 8 % hkv == 0) ? kCUsPerXCD * (8 / hkv) : kCUsPerXCD;
+  if (total * hkv <= resident) {
+    for (int64_t t0 = tier; t0 < total; t0 += 2 * tier)
+      std::reverse(plan + t0, plan + std::min<int64_t>(t0 + tier, total));
+  }
+  *num_items = static_cast<int32_t>(total);
+  return PA_OK;
+}
+
+pa_status pa_prefill_planned(const pa_pool* pool, const void* q, const void* k_rows,
+                             const void* v_rows, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_rows, int32_t max_chunk, const int32_t* query_start,
+                             const int32_t* block_tables, int32_t max_pages_per_seq,
+                             const int32_t* context_lens, float scale, float* out,
+                             const int32_t* plan, int32_t num_items, void* stream) {
+  if (!pool) return PA_ERR_NULL;
+  if (!plan && num_items > 0) return PA_ERR_NULL;
+  return prefill_impl(pool, q, k_rows, v_rows, num_seqs, num_q_heads, num_rows, max_chunk, query_start,
+                      block_tables, max_pages_per_seq, context_lens, scale, out, plan, num_items, stream);
 }
 
 pa_status pa_profile_start(void) {

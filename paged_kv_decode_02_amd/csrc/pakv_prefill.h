@@ -57,6 +57,10 @@ struct PrefillArgs {
   int32_t max_chunk;            // host bound on every chunk's length
   int32_t row_blocks;           // 128-row blocks per (sequence, KV head) in the grid
   float scale_log2;
+  // optional launch plan: workgroup (item, KV head) takes row block
+  // plan[item] = b | rb << 20; NULL = every (sequence, row block) in the
+  // rotated order below
+  const int32_t* plan;
 };
 
 struct WriteArgs {
@@ -363,7 +367,9 @@ __host__ __device__ constexpr int prefill_block_rows() { return 64 * prefill_row
 // rotation, whenever the sequence count divides 32 those are row blocks of
 // one sequence, and the CU that draws the longest cache does its four
 // longest blocks while others idle. With it, a CU's four blocks belong to
-// four sequences (8 sequences: offsets 0, 5, 2, 7). Wave w of a block
+// four sequences (8 sequences: offsets 0, 5, 2, 7). A launch plan made on
+// the host from the chunk and cache lengths (pa_prefill_plan) replaces this
+// order with one by work. Wave w of a block
 // takes rows w * 32 .. w * 32 + 31 in two groups of 16. The 4 waves share
 // every K/V tile: per page pair the workgroup loads K and V once (16-byte
 // loads, each thread its share), stores them to LDS in matrix-core operand
@@ -398,9 +404,17 @@ __global__ __launch_bounds__(256, prefill_occupancy<D>()) void prefill_kernel(Pr
   const int grp = lane >> 4;
   const int kvh = blockIdx.x % a.num_kv_heads;
   const int rest = blockIdx.x / a.num_kv_heads;
-  const int rbp = rest / a.num_seqs;
-  const int b = (rest % a.num_seqs + rbp + rbp / 4) % a.num_seqs;
-  const int rb = a.row_blocks - 1 - rbp;
+  int b, rb;
+  if (a.plan) {
+    const uint32_t item = (uint32_t)a.plan[rest];
+    b = (int)(item & 0xFFFFFu);
+    rb = (int)(item >> 20);
+    if (b >= a.num_seqs || rb >= a.row_blocks) return;
+  } else {
+    const int rbp = rest / a.num_seqs;
+    b = (rest % a.num_seqs + rbp + rbp / 4) % a.num_seqs;
+    rb = a.row_blocks - 1 - rbp;
+  }
   const int G = a.group;
   const Chunk ch = load_chunk(a.query_start, a.ctx_before, b, a.num_rows, a.max_chunk, a.stride);
   const int rows = ch.n * G;

@@ -285,3 +285,117 @@ def test_plan_tiers_reversed_only_when_the_grid_fits_at_once():
     got = B.decode_plan(pool, large, 64)
     assert got.tolist() == sorted(range(200), key=lambda b: (-(-(-int(large[b]) // 16)), b))
     B.lib().pa_pool_destroy(h)
+
+
+def expected_prefill_plan(ctx, chunks, hq, hkv, stride, max_chunk, d=64):
+    """Every row block of 128 query rows that holds rows, costed by the page
+    pairs its last row can see, largest first (ties: the later row block, then
+    the sequence); when the grid fits the device at once (items x kv heads <=
+    256 CUs x prefill workgroups per CU: 4 at d = 64, 1 at d = 128), every
+    other tier of 32 x 8 / kv_heads items is reversed."""
+    g = hq // hkv
+    block_rows = 128
+    row_blocks = (max_chunk * g + block_rows - 1) // block_rows
+    items = []
+    for rb in range(row_blocks - 1, -1, -1):
+        for b in range(len(ctx)):
+            c = min(max(int(ctx[b]), 0), stride * 16)
+            n = min(max(int(chunks[b]), 0), max_chunk, stride * 16 - c)
+            rows = n * g
+            if rb * block_rows >= rows:
+                continue
+            last = c + min(rb * block_rows + block_rows - 1, rows - 1) // g
+            pages = (last + 16) // 16
+            items.append(((pages + 1) // 2, b | (rb << 20)))
+    items.sort(key=lambda t: -t[0])          # stable: keeps the visiting order among ties
+    out = [code for _, code in items]
+    tier = 32 * (8 // hkv)
+    if len(out) * hkv <= 256 * (4 if d == 64 else 1):
+        for t0 in range(tier, len(out), 2 * tier):
+            out[t0:t0 + tier] = out[t0:t0 + tier][::-1]
+    return out
+
+
+@pytest.mark.parametrize("d,hq,hkv", [(64, 32, 8), (64, 8, 2), (128, 28, 4)])
+def test_prefill_plan_matches_its_definition(d, hq, hkv):
+    import numpy as np
+    L = B.lib()
+    h = make_pool(hkv=hkv, d=d)
+    pool = type("P", (), {"handle": h})()
+    rng = np.random.default_rng(11 + d + hkv)
+    for n_seq, max_chunk, stride in ((8, 512, 300), (3, 40, 10), (20, 2048, 200), (1, 4096, 300)):
+        ctx = rng.integers(-2, stride * 16 + 30, n_seq).astype(np.int32)
+        chunks = rng.integers(-1, max_chunk + 20, n_seq).astype(np.int32)
+        ctx[0], chunks[0] = 0, max_chunk                 # a fresh prompt at the bound
+        got = B.prefill_plan(pool, ctx, chunks, hq, stride, max_chunk)
+        assert got.tolist() == expected_prefill_plan(ctx, chunks, hq, hkv, stride, max_chunk, d)
+        cap = L.pa_prefill_plan_capacity(h, n_seq, hq, max_chunk)
+        assert cap == n_seq * ((max_chunk * (hq // hkv) + 127) // 128)
+        # every item once: (sequence, row block) pairs are distinct
+        assert len(set(got.tolist())) == len(got) <= cap
+    L.pa_pool_destroy(h)
+
+
+def test_prefill_plan_reverses_tiers_only_for_one_round_grids():
+    import numpy as np
+    h = make_pool(d=64)                       # 8 KV heads, 4 prefill workgroups per CU: 1024 resident
+    pool = type("P", (), {"handle": h})()
+    ctx = np.array([1457, 685, 1980, 3331, 2261, 890, 373, 4030], np.int32)
+    one = B.prefill_plan(pool, ctx, np.full(8, 512, np.int32), 32, 300, 512)   # 128 items x 8 = 1024
+    assert len(one) == 128
+    plain = expected_prefill_plan(ctx, [512] * 8, 32, 8, 300, 512)
+    assert one.tolist() == plain
+    costs = {}
+    for b in range(8):
+        for rb in range(16):
+            last = int(ctx[b]) + min(rb * 128 + 127, 2047) // 4
+            costs[b | (rb << 20)] = ((last + 16) // 16 + 1) // 2
+    c = [costs[x] for x in one.tolist()]
+    assert c[:32] == sorted(c[:32], reverse=True) and c[32:64] == sorted(c[32:64])
+    assert c[64:96] == sorted(c[64:96], reverse=True) and c[96:] == sorted(c[96:])
+    # 256 items x 8 = 2048 workgroups: two rounds, so plain largest-first order
+    many = B.prefill_plan(pool, ctx, np.full(8, 1024, np.int32), 32, 400, 1024)
+    last_pos = lambda x: int(ctx[x & 0xFFFFF]) + min((x >> 20) * 128 + 127, 4095) // 4
+    pairs = [((last_pos(x) + 16) // 16 + 1) // 2 for x in many.tolist()]
+    assert len(many) == 256 and pairs == sorted(pairs, reverse=True)
+    B.lib().pa_pool_destroy(h)
+
+
+def test_prefill_plan_and_planned_validation():
+    import numpy as np
+    L = B.lib()
+    h = make_pool(d=64)
+    n = ctypes.c_int32(-1)
+    ctx = np.array([100, 5000, 0], dtype=np.int32)
+    chunks = np.array([64, 0, 300], dtype=np.int32)
+    buf = np.zeros(16, dtype=np.int32)
+    assert L.pa_prefill_plan_capacity(None, 3, 32, 300) == -1
+    assert L.pa_prefill_plan_capacity(h, 3, 12, 300) == -1           # not a multiple of 8 KV heads
+    assert L.pa_prefill_plan_capacity(h, 3, 8 * 17, 300) == -1       # 17 query heads per KV head
+    assert L.pa_prefill_plan_capacity(h, (1 << 20) + 1, 32, 1) == -1
+    assert L.pa_prefill_plan_capacity(h, 1, 32, 32 * 2048 + 1) == -1  # more than 2^11 row blocks
+    assert L.pa_prefill_plan_capacity(h, 3, 32, 300) == 3 * 10
+    args = lambda cap, out=buf.ctypes.data, nptr=ctypes.byref(n), c=ctx.ctypes.data, k=chunks.ctypes.data: \
+        L.pa_prefill_plan(h, c, k, 3, 32, 400, 300, out, cap, nptr)
+    assert args(16, nptr=None) == NULL
+    assert args(16, c=None) == NULL
+    assert args(16, k=None) == NULL
+    assert args(16, out=None) == NULL
+    # rows: 64 x 4 = 256 (2 blocks), 0, 300 x 4 = 1200 (10 blocks): 12 items
+    assert args(11) == INVALID
+    assert args(16) == OK and n.value == 12
+    assert L.pa_prefill_plan(h, None, None, 0, 32, 400, 300, None, 0, ctypes.byref(n)) == OK and n.value == 0
+    assert L.pa_prefill_plan(h, ctx.ctypes.data, chunks.ctypes.data, 3, 32, 0, 300, buf.ctypes.data, 16,
+                             ctypes.byref(n)) == INVALID
+
+    def pre(plan=P, items=4, num_seqs=2, max_chunk=8):
+        return L.pa_prefill_planned(h, P, P, P, num_seqs, 32, 10, max_chunk, P, P, 4, P, 0.125, P2, plan,
+                                    items, None)
+
+    assert pre(plan=None) == NULL
+    assert pre(plan=P + 2) == ALIGN
+    assert pre(items=-1) == INVALID
+    assert pre(items=2 * 1 + 1) == INVALID     # 2 sequences x 1 row block of 8 x 4 rows
+    assert pre(num_seqs=0, plan=None, items=0) == OK
+    assert L.pa_prefill_planned(None, P, P, P, 1, 32, 1, 1, P, P, 1, P, 0.1, P2, P, 1, None) == NULL
+    L.pa_pool_destroy(h)

@@ -36,6 +36,15 @@ class PrefillCase:
         return B.prefill(self.pool, self.q_dev, self.kr_dev, self.vr_dev, self.qs_dev, self.bt_dev,
                          self.bef_dev, float(self.scale), self.max_chunk if max_chunk is None else max_chunk)
 
+    def run_planned(self):
+        """pa_prefill_planned with the host-made plan for this case's lengths."""
+        import torch
+        plan = B.prefill_plan(self.pool, self.bef, np.diff(self.qs), self.q.shape[1], self.bt.shape[1],
+                              self.max_chunk)
+        plan_dev = torch.from_numpy(plan).to(self.q_dev.device)
+        return B.prefill_planned(self.pool, self.q_dev, self.kr_dev, self.vr_dev, self.qs_dev, self.bt_dev,
+                                 self.bef_dev, float(self.scale), self.max_chunk, plan_dev)
+
     def pools(self):
         return (self.k_dev.cpu().numpy().view(np.uint16), self.v_dev.cpu().numpy().view(np.uint16))
 
@@ -73,6 +82,9 @@ def test_prefill_matches_oracle(label, hq, hkv, d, befores, chunks):
     # a looser grid bound changes nothing; a second run gives the same bits
     again = c.run(max_chunk=c.max_chunk + 37).cpu().numpy()
     assert np.array_equal(again, out), f"{label}: result depends on the grid bound or the run"
+    # the launch plan changes only the order of the row blocks
+    planned = c.run_planned().cpu().numpy()
+    assert np.array_equal(planned, out), f"{label}: pa_prefill_planned differs from pa_prefill"
     log(f"prefill {label}: max abs {a:.2e} max rel {r:.2e}")
 
 
@@ -147,10 +159,11 @@ def test_prefill_any_scale(scale):
 @pytest.mark.parametrize("name", ["prefill", "prefill_d128", "prefill_chunked"])
 def test_prefill_workload_full_size_sampled(name):
     """The benchmark's prefill workloads at full size, launched as the
-    benchmark launches them (one pa_prefill per layer over the whole batch):
-    on sampled sequences of the first and last layer, the pages after the
-    chunk write equal the oracle's write bit for bit, and sampled chunk rows
-    (always the first and the last) match the oracle computed row by row."""
+    benchmark launches them (one pa_prefill_planned per layer over the whole
+    batch, with the host-made plan): the same bits as pa_prefill; on sampled
+    sequences of the first and last layer, the pages after the chunk write
+    equal the oracle's write bit for bit, and sampled chunk rows (always the
+    first and the last) match the oracle computed row by row."""
     import torch
     from paged_kv_decode_02_amd import workloads as W
     dev = device()
@@ -164,10 +177,18 @@ def test_prefill_workload_full_size_sampled(name):
     q, k_rows, v_rows = w.rows_device("q", dev), w.rows_device("k", dev), w.rows_device("v", dev)
     g = base.num_q_heads // base.num_kv_heads
     rng = np.random.default_rng(31)
+    max_chunk = int(w.chunks.max())
+    plan = torch.from_numpy(B.prefill_plan(pool, w.ctx_before, w.chunks, base.num_q_heads,
+                                           base.block_tables.shape[2], max_chunk)).to(dev)
     for layer in sorted({0, base.num_layers - 1}):
-        log(f"{name}: layer {layer}, {w.num_rows} rows, before={w.ctx_before.tolist()} entry=pa_prefill")
-        out = B.prefill(pool, q[layer], k_rows[layer], v_rows[layer], qs, bt[layer], before,
-                        float(base.scale), int(w.chunks.max())).cpu().numpy()
+        log(f"{name}: layer {layer}, {w.num_rows} rows, before={w.ctx_before.tolist()} "
+            f"entry=pa_prefill_planned ({plan.numel()} items)")
+        out = B.prefill_planned(pool, q[layer], k_rows[layer], v_rows[layer], qs, bt[layer], before,
+                                float(base.scale), max_chunk, plan).cpu().numpy()
+        plain = B.prefill(pool, q[layer], k_rows[layer], v_rows[layer], qs, bt[layer], before,
+                          float(base.scale), max_chunk).cpu().numpy()
+        assert np.array_equal(plain, out), f"{name} layer {layer}: pa_prefill_planned != pa_prefill"
+        del plain
         for b in sorted(rng.choice(len(w.chunks), size=min(3, len(w.chunks)), replace=False).tolist()):
             n_tot = int(w.ctx_before[b]) + int(w.chunks[b])
             pages = base.block_tables[layer, b, :-(-n_tot // 16)].astype(np.int64)
