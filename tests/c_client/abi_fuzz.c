@@ -6,6 +6,11 @@
  *     (sequence, split) appears once (an empty context once, as split 0),
  *     page counts never increase along the plan outside the reversed tiers
  *     of a one-round grid, and a capacity one short is refused untouched;
+ *   - pa_prefill_plan on random cache and chunk lengths (negative and past
+ *     the bounds included): every row block that holds rows appears once
+ *     and no other, costs never increase along the plan outside the
+ *     reversed tiers of a one-round grid, and a capacity one short is
+ *     refused;
  *   - the sizing calls and pa_status_str over every code and beyond;
  *   - the argument checks of every entry point that queues work, always with
  *     an argument they must refuse, so nothing reaches the HIP runtime.
@@ -103,6 +108,71 @@ static void plan_round(long round) {
   pa_pool_destroy(pool);
 }
 
+static void prefill_plan_round(long round) {
+  const int d = rnd(2) ? 64 : 128;
+  static const int kv_choices[4] = {1, 2, 4, 8};
+  const int hkv = kv_choices[rnd(4)];
+  const int group = 1 + (int)rnd(16);
+  const int hq = hkv * group;
+  pa_pool* pool = NULL;
+  if (pa_pool_create(&pool, DEV, DEV, 1 + (int)rnd(100000), 16, hkv, d) != PA_OK) fail("pool", round);
+  const int32_t num_seqs = (int32_t)rnd(40);
+  const int32_t stride = 1 + (int32_t)rnd(400);
+  const int32_t max_chunk = (int32_t)rnd(rnd(4) ? 700 : 5000);
+  const int64_t cap = pa_prefill_plan_capacity(pool, num_seqs, hq, max_chunk);
+  const int64_t row_blocks = ((int64_t)max_chunk * group + 127) / 128;
+  if (cap != (int64_t)num_seqs * row_blocks) fail("prefill capacity", round);
+  int32_t* ctx = (int32_t*)malloc(sizeof(int32_t) * (size_t)(num_seqs ? num_seqs : 1));
+  int32_t* chunk = (int32_t*)malloc(sizeof(int32_t) * (size_t)(num_seqs ? num_seqs : 1));
+  if (!ctx || !chunk) fail("oom", round);
+  int64_t need = 0;
+  for (int b = 0; b < num_seqs; ++b) {
+    const uint32_t k = rnd(8);
+    ctx[b] = k == 0 ? -(int32_t)rnd(50) : k == 1 ? stride * 16 + (int32_t)rnd(100) : (int32_t)rnd((uint32_t)stride * 16 + 1);
+    chunk[b] = k == 2 ? -(int32_t)rnd(50) : k == 3 ? max_chunk + (int32_t)rnd(100) : (int32_t)rnd((uint32_t)max_chunk + 1);
+    const int64_t c = ctx[b] < 0 ? 0 : (ctx[b] > stride * 16 ? stride * 16 : ctx[b]);
+    int64_t n = chunk[b] < 0 ? 0 : (chunk[b] > max_chunk ? max_chunk : chunk[b]);
+    if (n > stride * 16 - c) n = stride * 16 - c;
+    need += (n * group + 127) / 128;
+  }
+  int32_t* plan = (int32_t*)malloc(sizeof(int32_t) * (size_t)(need ? need : 1));
+  if (!plan) fail("oom", round);
+  int32_t items = -1;
+  if (need > 0 &&
+      pa_prefill_plan(pool, ctx, chunk, num_seqs, hq, stride, max_chunk, plan, need - 1, &items) == PA_OK)
+    fail("prefill short capacity", round);
+  if (pa_prefill_plan(pool, ctx, chunk, num_seqs, hq, stride, max_chunk, plan, need, &items) != PA_OK)
+    fail("prefill plan", round);
+  if (items != need) fail("prefill item count", round);
+  char* seen = (char*)calloc((size_t)(num_seqs ? num_seqs : 1) * (size_t)(row_blocks ? row_blocks : 1), 1);
+  if (!seen) fail("oom", round);
+  int64_t prev = INT64_MAX;
+  int breaks = 0;
+  for (int32_t i = 0; i < items; ++i) {
+    const uint32_t it = (uint32_t)plan[i];
+    const int b = (int)(it & 0xFFFFFu);
+    const int64_t rb = (int64_t)(it >> 20);
+    if (b >= num_seqs || rb >= row_blocks) fail("prefill item out of range", round);
+    if (seen[(size_t)b * row_blocks + rb]++) fail("prefill item twice", round);
+    const int64_t c = ctx[b] < 0 ? 0 : (ctx[b] > stride * 16 ? stride * 16 : ctx[b]);
+    int64_t n = chunk[b] < 0 ? 0 : (chunk[b] > max_chunk ? max_chunk : chunk[b]);
+    if (n > stride * 16 - c) n = stride * 16 - c;
+    const int64_t rows = n * group;
+    if (rb * 128 >= rows) fail("prefill item past the chunk", round);
+    const int64_t last = c + ((rb * 128 + 127 < rows - 1 ? rb * 128 + 127 : rows - 1) / group);
+    const int64_t pairs = ((last + 16) / 16 + 1) / 2;
+    if (pairs > prev) ++breaks;
+    prev = pairs;
+  }
+  /* 256 CUs x prefill workgroups per CU (4 at head_dim 64, 1 at 128) */
+  if (breaks > 0 && (int64_t)items * hkv > 256 * (d == 64 ? 4 : 1)) fail("prefill plan order", round);
+  free(seen);
+  free(plan);
+  free(chunk);
+  free(ctx);
+  pa_pool_destroy(pool);
+}
+
 static void validation_round(long round) {
   pa_pool* pool = NULL;
   const int d = rnd(2) ? 64 : 128;
@@ -170,6 +240,7 @@ int main(int argc, char** argv) {
   if (pa_decode_plan(NULL, NULL, 0, 1, NULL, 0, &items) != PA_ERR_NULL) fail("plan NULL", -1);
   for (long r = 0; r < rounds; ++r) {
     plan_round(r);
+    prefill_plan_round(r);
     validation_round(r);
   }
   printf("abi_fuzz: %ld rounds: ok\n", rounds);

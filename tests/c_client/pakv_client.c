@@ -9,8 +9,10 @@
  *   - the page pool is uploaded from k_pool.bin / v_pool.bin;
  *   - a scheduler (continuous batching) over the pool admits the requests of
  *     config.txt;
- *   - their prompts are prefilled with pa_prefill, layer by layer
- *     (prefill_{q,k,v}_<layer>.bin in, prefill_out_<layer>.bin out);
+ *   - their prompts are prefilled layer by layer, layer 0 through a launch
+ *     plan (pa_prefill_plan + pa_prefill_planned), the other layers through
+ *     pa_prefill (prefill_{q,k,v}_<layer>.bin in, prefill_out_<layer>.bin
+ *     out);
  *   - then `steps` decode steps: per layer pa_kv_append of the new token
  *     (step<s>_{k,v}_<layer>.bin), then attention, layer 0 through a launch
  *     plan (pa_decode_plan + pa_decode_planned), the other layers through
@@ -114,6 +116,7 @@ int main(int argc, char** argv) {
   int P, Hkv, Hq, D, L, MB, stride, steps, nreq;
   if (fscanf(f, "%d %d %d %d %d %d %d %d %d", &P, &Hkv, &Hq, &D, &L, &MB, &stride, &steps, &nreq) != 9)
     die("bad config header");
+  if (MB < 1 || MB > 64) die("max_batch must be in 1..64 (fixed-size host arrays)");
   if (nreq < 1 || nreq > MB) die("bad request count");
   int prompt[64], max_new[64];
   for (int i = 0; i < nreq; ++i)
@@ -172,6 +175,18 @@ int main(int argc, char** argv) {
   float* out_dev = (float*)dev_alloc((size_t)(N > MB ? N : MB) * Hq * D * 4);
   float* out_host = (float*)malloc((size_t)(N > MB ? N : MB) * Hq * D * 4);
   if (!out_host) die("out of memory");
+  /* the prefill launch plan from the host's cache and chunk lengths */
+  int32_t chunk_host[64];
+  for (int b = 0; b < MB; ++b) chunk_host[b] = qs[b + 1] - qs[b];
+  const int64_t pplan_cap = pa_prefill_plan_capacity(pool, MB, Hq, max_chunk);
+  if (pplan_cap < 0) die("pa_prefill_plan_capacity");
+  int32_t* pplan = (int32_t*)malloc((size_t)(pplan_cap > 0 ? pplan_cap : 1) * 4);
+  if (!pplan) die("out of memory");
+  int32_t pplan_items = 0;
+  check(pa_prefill_plan(pool, ctx_host, chunk_host, MB, Hq, stride, max_chunk, pplan, pplan_cap, &pplan_items),
+        "pa_prefill_plan");
+  int32_t* pplan_dev = (int32_t*)dev_alloc((size_t)(pplan_items > 0 ? pplan_items : 1) * 4);
+  upload(pplan_dev, pplan, (size_t)pplan_items * 4);
   for (int l = 0; l < L; ++l) {
     char name[256];
     for (size_t e = 0; e < bt_layer; ++e) bt_clean[e] = bt_host[l * bt_layer + e] < 0 ? 0 : bt_host[l * bt_layer + e];
@@ -182,9 +197,14 @@ int main(int argc, char** argv) {
     void* kr = dev_from_file(name, (size_t)N * Hkv * D * 2);
     snprintf(name, sizeof name, "prefill_v_%d.bin", l);
     void* vr = dev_from_file(name, (size_t)N * Hkv * D * 2);
-    check(pa_prefill(pool, q, kr, vr, MB, Hq, N, max_chunk, qs_dev, bt_dev, stride, ctx_dev, scale,
-                     out_dev, NULL),
-          "pa_prefill");
+    if (l == 0)
+      check(pa_prefill_planned(pool, q, kr, vr, MB, Hq, N, max_chunk, qs_dev, bt_dev, stride, ctx_dev,
+                               scale, out_dev, pplan_dev, pplan_items, NULL),
+            "pa_prefill_planned");
+    else
+      check(pa_prefill(pool, q, kr, vr, MB, Hq, N, max_chunk, qs_dev, bt_dev, stride, ctx_dev, scale,
+                       out_dev, NULL),
+            "pa_prefill");
     hip_check(hipDeviceSynchronize(), "prefill");
     download(out_host, out_dev, (size_t)N * Hq * D * 4);
     snprintf(name, sizeof name, "prefill_out_%d.bin", l);
@@ -267,9 +287,11 @@ int main(int argc, char** argv) {
   pa_pool_destroy(pool);
   free(pool_host);
   free(plan);
+  free(pplan);
   free(out_host);
   free(bt_clean);
   hip_check(hipFree(plan_dev), "hipFree");
+  hip_check(hipFree(pplan_dev), "hipFree");
   hip_check(hipFree(ws), "hipFree");
   hip_check(hipFree(out_dev), "hipFree");
   hip_check(hipFree(qs_dev), "hipFree");
