@@ -85,7 +85,8 @@ typedef enum pa_status
 {
   PA_OK = 0,
   PA_ERR_NULL = 1,        /* a required pointer is NULL */
-  PA_ERR_INVALID = 2,     /* a count or size is out of range */
+  PA_ERR_INVALID = 2,     /* a count or size is out of range (also: the host could not
+                             allocate the memory a descriptor or a plan needs) */
   PA_ERR_UNSUPPORTED = 3, /* valid in principle, not built: head_dim, page size, group size */
   PA_ERR_ALIGN = 4,       /* a device pointer is not aligned as documented below */
   PA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than pa_decode_workspace_bytes */

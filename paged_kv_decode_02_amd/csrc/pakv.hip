@@ -123,7 +123,12 @@ struct LaunchTimer {
   ~LaunchTimer() {
     if (!g_profiling || !rec.start) return;
     (void)hipEventRecord(rec.stop, stream);
-    g_records.push_back(rec);
+    try {
+      g_records.push_back(rec);
+    } catch (...) {   // out of host memory: this launch goes untimed
+      (void)hipEventDestroy(rec.start);
+      (void)hipEventDestroy(rec.stop);
+    }
   }
 };
 
@@ -326,6 +331,10 @@ int64_t pa_decode_plan_capacity(const pa_pool* pool, int32_t num_seqs, int32_t m
   return static_cast<int64_t>(num_seqs) * s_max;
 }
 
+static pa_status decode_plan_impl(const pa_pool* pool, const int32_t* context_lens_host, int32_t num_seqs,
+                                  int32_t max_pages_per_seq, int32_t* plan, int64_t capacity,
+                                  int32_t* num_items);
+
 pa_status pa_decode_plan(const pa_pool* pool, const int32_t* context_lens_host, int32_t num_seqs,
                          int32_t max_pages_per_seq, int32_t* plan, int64_t capacity,
                          int32_t* num_items) {
@@ -335,6 +344,18 @@ pa_status pa_decode_plan(const pa_pool* pool, const int32_t* context_lens_host, 
   if (cap_needed < 0) return PA_ERR_INVALID;
   if (num_seqs == 0) return PA_OK;
   if (!context_lens_host || !plan) return PA_ERR_NULL;
+  try {
+    return decode_plan_impl(pool, context_lens_host, num_seqs, max_pages_per_seq, plan, capacity,
+                            num_items);
+  } catch (...) {   // out of host memory; nothing escapes the C ABI
+    *num_items = 0;
+    return PA_ERR_INVALID;
+  }
+}
+
+static pa_status decode_plan_impl(const pa_pool* pool, const int32_t* context_lens_host, int32_t num_seqs,
+                                  int32_t max_pages_per_seq, int32_t* plan, int64_t capacity,
+                                  int32_t* num_items) {
   const int sp = split_pages(pool->head_dim);
   const int64_t max_tok = static_cast<int64_t>(max_pages_per_seq) * pakv::kPage;
   // pages of every split, then a counting sort by page count, largest first
@@ -554,6 +575,11 @@ int64_t pa_prefill_plan_capacity(const pa_pool* pool, int32_t num_seqs, int32_t 
   return static_cast<int64_t>(num_seqs) * row_blocks;
 }
 
+static pa_status prefill_plan_impl(const pa_pool* pool, const int32_t* context_lens_host,
+                                   const int32_t* chunk_lens_host, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t max_pages_per_seq, int32_t max_chunk, int32_t* plan,
+                                   int64_t capacity, int32_t* num_items);
+
 pa_status pa_prefill_plan(const pa_pool* pool, const int32_t* context_lens_host,
                           const int32_t* chunk_lens_host, int32_t num_seqs, int32_t num_q_heads,
                           int32_t max_pages_per_seq, int32_t max_chunk, int32_t* plan,
@@ -565,6 +591,19 @@ pa_status pa_prefill_plan(const pa_pool* pool, const int32_t* context_lens_host,
   if (pa_prefill_plan_capacity(pool, num_seqs, num_q_heads, max_chunk) < 0) return PA_ERR_INVALID;
   if (num_seqs == 0 || max_chunk == 0) return PA_OK;
   if (!context_lens_host || !chunk_lens_host || !plan) return PA_ERR_NULL;
+  try {
+    return prefill_plan_impl(pool, context_lens_host, chunk_lens_host, num_seqs, num_q_heads,
+                             max_pages_per_seq, max_chunk, plan, capacity, num_items);
+  } catch (...) {   // out of host memory; nothing escapes the C ABI
+    *num_items = 0;
+    return PA_ERR_INVALID;
+  }
+}
+
+static pa_status prefill_plan_impl(const pa_pool* pool, const int32_t* context_lens_host,
+                                   const int32_t* chunk_lens_host, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t max_pages_per_seq, int32_t max_chunk, int32_t* plan,
+                                   int64_t capacity, int32_t* num_items) {
   const int d = pool->head_dim;
   const int group = num_q_heads / pool->num_kv_heads;
   const int block_rows = d == 64 ? pakv::prefill_block_rows<64>() : pakv::prefill_block_rows<128>();
