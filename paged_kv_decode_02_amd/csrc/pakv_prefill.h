@@ -212,10 +212,21 @@ struct PrefillWave {
   bf16x8 qf[RG][D / 32];  // the lane's query row per row group, B operand
 };
 
+// The page ids of a pair are the same for every lane, and the block tables
+// do not change during the launch: read through the constant address space
+// they are scalar loads (both issued before either is used), and the clamp
+// into the pool and the pages' addresses are scalar arithmetic, not per-lane
+// 64-bit multiplies.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+
 template <int D, int RG>
-__device__ __forceinline__ int clamp_pid(const PrefillWave<D, RG>& w, int logical) {
-  const int p = w.bt_row[logical];
-  return p < 0 ? 0 : (p >= w.num_pages ? w.num_pages - 1 : p);
+__device__ __forceinline__ void pair_pages(const PrefillWave<D, RG>& w, int first, int second, int& pa,
+                                           int& pb) {
+  const const_i32_ptr row = (const_i32_ptr)(uintptr_t)w.bt_row;
+  const int ra = row[first];
+  const int rb = row[second];
+  pa = ra < 0 ? 0 : (ra >= w.num_pages ? w.num_pages - 1 : ra);
+  pb = rb < 0 ? 0 : (rb >= w.num_pages ? w.num_pages - 1 : rb);
 }
 
 // Maximum over the 4 lanes that hold one row (l, l ^ 16, l ^ 32, l ^ 48),
@@ -490,12 +501,16 @@ __global__ __launch_bounds__(256, prefill_occupancy<D>()) void prefill_kernel(Pr
   }
   u32x4 sk[NPT], sv[NPT];
   auto gload = [&](int pr) {
-    const int pa = clamp_pid(w, 2 * pr);
-    const int pb = clamp_pid(w, min(2 * pr + 1, blk_pages - 1));
+    int pa, pb;
+    pair_pages(w, 2 * pr, min(2 * pr + 1, blk_pages - 1), pa, pb);
+    const uint16_t* ka = w.ktile + (size_t)pa * w.page_elems;
+    const uint16_t* kb = w.ktile + (size_t)pb * w.page_elems;
+    const uint16_t* va = w.vtile + (size_t)pa * w.page_elems;
+    const uint16_t* vb = w.vtile + (size_t)pb * w.page_elems;
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-      sk[i] = *(const u32x4*)(w.ktile + (size_t)(kp2[i] ? pb : pa) * w.page_elems + kg[i]);
-      sv[i] = *(const u32x4*)(w.vtile + (size_t)(vp2[i] ? pb : pa) * w.page_elems + vg[i]);
+      sk[i] = *(const u32x4*)((kp2[i] ? kb : ka) + kg[i]);
+      sv[i] = *(const u32x4*)((vp2[i] ? vb : va) + vg[i]);
     }
   };
   auto lstore = [&](int bufi) {
