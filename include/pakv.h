@@ -269,7 +269,7 @@ pa_status pa_prefill(const pa_pool* pool, const void* q, const void* k_rows, con
  * can order the row blocks by that cost instead, largest first, leaving out
  * the blocks past each chunk's end: when the whole grid fits the device at
  * once (row blocks x num_kv_heads <= 256 CUs x the prefill workgroups a CU
- * holds: 4 at head_dim 64, 1 at 128), every other tier of row blocks that
+ * holds: 4 at head_dim 64, 2 at 128), every other tier of row blocks that
  * the CUs of one XCD take in turn is reversed, pairing large blocks with
  * small ones on each CU, as pa_decode_plan does for splits.
  *

@@ -362,9 +362,11 @@ template <int D>
 __host__ __device__ constexpr int prefill_row_groups() { return 2; }
 // Waves per SIMD: 4 at d = 64 (128 registers per lane, a few spilled; more
 // waves overlap one wave's softmax with another's matrix-core work and
-// measured faster than 2 or 3), 1 at d = 128 (2 measured the same).
+// measured faster than 2 or 3), 2 at d = 128 (at most 256 registers per
+// lane; the kernel needs about 220, so a bound of 1 gave 2 waves as well).
+// The launch plan counts on these as the workgroups a CU holds.
 template <int D>
-__host__ __device__ constexpr int prefill_occupancy() { return D == 64 ? 4 : 1; }
+__host__ __device__ constexpr int prefill_occupancy() { return D == 64 ? 4 : 2; }
 // rows per workgroup: 4 waves x 16 rows x row groups
 template <int D>
 __host__ __device__ constexpr int prefill_block_rows() { return 64 * prefill_row_groups<D>(); }

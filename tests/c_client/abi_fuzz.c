@@ -164,8 +164,8 @@ static void prefill_plan_round(long round) {
     if (pairs > prev) ++breaks;
     prev = pairs;
   }
-  /* 256 CUs x prefill workgroups per CU (4 at head_dim 64, 1 at 128) */
-  if (breaks > 0 && (int64_t)items * hkv > 256 * (d == 64 ? 4 : 1)) fail("prefill plan order", round);
+  /* 256 CUs x prefill workgroups per CU (4 at head_dim 64, 2 at 128) */
+  if (breaks > 0 && (int64_t)items * hkv > 256 * (d == 64 ? 4 : 2)) fail("prefill plan order", round);
   free(seen);
   free(plan);
   free(chunk);

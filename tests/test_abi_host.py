@@ -291,7 +291,7 @@ def expected_prefill_plan(ctx, chunks, hq, hkv, stride, max_chunk, d=64):
     """Every row block of 128 query rows that holds rows, costed by the page
     pairs its last row can see, largest first (ties: the later row block, then
     the sequence); when the grid fits the device at once (items x kv heads <=
-    256 CUs x prefill workgroups per CU: 4 at d = 64, 1 at d = 128), every
+    256 CUs x prefill workgroups per CU: 4 at d = 64, 2 at d = 128), every
     other tier of 32 x 8 / kv_heads items is reversed."""
     g = hq // hkv
     block_rows = 128
@@ -310,7 +310,7 @@ def expected_prefill_plan(ctx, chunks, hq, hkv, stride, max_chunk, d=64):
     items.sort(key=lambda t: -t[0])          # stable: keeps the visiting order among ties
     out = [code for _, code in items]
     tier = 32 * (8 // hkv)
-    if len(out) * hkv <= 256 * (4 if d == 64 else 1):
+    if len(out) * hkv <= 256 * (4 if d == 64 else 2):
         for t0 in range(tier, len(out), 2 * tier):
             out[t0:t0 + tier] = out[t0:t0 + tier][::-1]
     return out
