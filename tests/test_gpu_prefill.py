@@ -88,6 +88,24 @@ def test_prefill_matches_oracle(label, hq, hkv, d, befores, chunks):
     log(f"prefill {label}: max abs {a:.2e} max rel {r:.2e}")
 
 
+def test_prefill_plan_items_out_of_range_are_skipped():
+    """A plan holding items that name a sequence or a row block past the grid
+    gives the same rows as pa_prefill (those items do nothing)."""
+    import torch
+    c = PrefillCase(77, 32, 8, 64, [17, 100, 16, 5], [64, 3, 33, 0])
+    log("prefill plan with out-of-range items: before=[17, 100, 16, 5] chunks=[64, 3, 33, 0]")
+    plain = c.run().cpu().numpy()
+    plan = B.prefill_plan(c.pool, c.bef, np.diff(c.qs), 32, c.bt.shape[1], c.max_chunk)
+    row_blocks = -(-c.max_chunk * 4 // 128)
+    bogus = np.array([4 + 5, row_blocks << 20], dtype=np.int32)       # sequence 9; row block past the grid
+    p = np.concatenate([plan, bogus])
+    assert p.size <= B.prefill_plan_capacity(c.pool, 4, 32, c.max_chunk)
+    out = torch.full((c.q.shape[0], 32, 64), float("nan"), device=c.q_dev.device)
+    B.prefill_planned(c.pool, c.q_dev, c.kr_dev, c.vr_dev, c.qs_dev, c.bt_dev, c.bef_dev, float(c.scale),
+                      c.max_chunk, torch.from_numpy(p).to(c.q_dev.device), out=out)
+    assert np.array_equal(out.cpu().numpy(), plain), "out-of-range plan items changed the result"
+
+
 def test_kv_write_alone_bit_exact():
     c = PrefillCase(5, 32, 8, 64, [0, 7, 31, 48], [40, 9, 1, 16])
     log("kv_write: before=[0,7,31,48] chunks=[40,9,1,16] entry=pa_kv_write")
