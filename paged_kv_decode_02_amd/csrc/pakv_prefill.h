@@ -265,19 +265,23 @@ __device__ __forceinline__ void prefill_compute(const PrefillWave<D, RG>& w, Pre
   // only a pair that some row of the wave cannot see whole needs the mask
   const bool diag = 32 * pr + 31 > w.first_pos;
   bf16x8 ph[RG], pl[RG];
+  // every row group's scores first, so that the matrix cores work on the
+  // next group's while the VALU does this group's weights
+  f32x4 scg[RG][2];
 #pragma unroll
-  for (int g = 0; g < RG; ++g) {
-    f32x4 sc[2];
+  for (int g = 0; g < RG; ++g)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      sc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      scg[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf.k[j][kk]), w.qf[g][kk], sc[j], 0, 0, 0);
+        scg[g][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf.k[j][kk]), w.qf[g][kk], scg[g][j], 0, 0, 0);
     }
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
     float sv[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sv[e] = sc[e >> 2][e & 3];
+    for (int e = 0; e < 8; ++e) sv[e] = scg[g][e >> 2][e & 3];
     if (diag) {
       const int lim = w.pos[g] - key0;     // key0 + e is visible iff e <= lim
 #pragma unroll
