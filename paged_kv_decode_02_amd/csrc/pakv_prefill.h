@@ -25,7 +25,8 @@
 //     of MFMA j mix the two pages (row r is page r / 8, slot
 //     8 ((r / 4) % 2) + 4 j + r % 4), so that lane (r = lane % 16,
 //     grp = lane / 16) ends up with slots 8 (grp % 2) + 0..7 of page grp / 2
-//     for row r: 8 consecutive keys, positions 32 pair + 8 grp + 0..7;
+//     for row r: 8 consecutive keys, positions 32 pair + 8 grp + 0..7
+//     (both row groups' scores are issued before either group's softmax);
 //   causal mask by select (only on pairs that cross the diagonal), FP32
 //     online softmax per row: weights against the running max as it stands;
 //     the row maxima (over the 4 lanes holding a row, by lane swaps) are
