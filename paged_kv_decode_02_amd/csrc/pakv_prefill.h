@@ -365,10 +365,11 @@ __device__ __forceinline__ void prefill_compute(const PrefillWave<D, RG>& w, Pre
 // Two groups of 16 rows per wave: every K/V operand loaded feeds both.
 template <int D>
 __host__ __device__ constexpr int prefill_row_groups() { return 2; }
-// Waves per SIMD: 4 at d = 64 (128 registers per lane, a few spilled; more
-// waves overlap one wave's softmax with another's matrix-core work and
-// measured faster than 2 or 3), 2 at d = 128 (at most 256 registers per
-// lane; the kernel needs about 220, so a bound of 1 gave 2 waves as well).
+// Waves per SIMD: 4 at d = 64 (at most 128 registers per lane, the kernel
+// needs 126; more waves overlap one wave's softmax with another's
+// matrix-core work and measured faster than 2 or 3), 2 at d = 128 (at most
+// 256 registers per lane, the kernel needs about 200; a bound of 1 gave 2
+// waves as well).
 // The launch plan counts on these as the workgroups a CU holds.
 template <int D>
 __host__ __device__ constexpr int prefill_occupancy() { return D == 64 ? 4 : 2; }
