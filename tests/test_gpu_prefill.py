@@ -106,6 +106,27 @@ def test_prefill_plan_items_out_of_range_are_skipped():
     assert np.array_equal(out.cpu().numpy(), plain), "out-of-range plan items changed the result"
 
 
+def test_prefill_batch_invariance_bitwise():
+    """A sequence's rows do not depend on the rest of the batch: each sequence
+    prefilled alone (same pages, same block-table row) gives the rows it got
+    inside the batch bit for bit, planned or not."""
+    import torch
+    befores, chunks = [0, 300, 17, 2100], [200, 45, 130, 64]
+    c = PrefillCase(91, 32, 8, 64, befores, chunks)
+    log(f"prefill batch invariance: before={befores} chunks={chunks}")
+    batch = c.run().cpu().numpy()
+    planned = c.run_planned().cpu().numpy()
+    assert np.array_equal(batch, planned)
+    dev = c.q_dev.device
+    for b in range(len(chunks)):
+        r0, r1 = int(c.qs[b]), int(c.qs[b + 1])
+        qs1 = torch.tensor([0, r1 - r0], dtype=torch.int32, device=dev)
+        out = B.prefill(c.pool, c.q_dev[r0:r1].contiguous(), c.kr_dev[r0:r1].contiguous(),
+                        c.vr_dev[r0:r1].contiguous(), qs1, c.bt_dev[b:b + 1].contiguous(),
+                        c.bef_dev[b:b + 1].contiguous(), float(c.scale), chunks[b])
+        assert np.array_equal(out.cpu().numpy(), batch[r0:r1]), f"sequence {b}: rows differ alone vs in the batch"
+
+
 def test_kv_write_alone_bit_exact():
     c = PrefillCase(5, 32, 8, 64, [0, 7, 31, 48], [40, 9, 1, 16])
     log("kv_write: before=[0,7,31,48] chunks=[40,9,1,16] entry=pa_kv_write")
