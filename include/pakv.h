@@ -146,7 +146,10 @@ int32_t pa_split_tokens(int32_t head_dim);
  * FP32 accumulation and FP32 online softmax. q: BF16 queries; num_q_heads a
  * multiple of the pool's num_kv_heads with at most 16 query heads per KV
  * head; block_tables / context_lens: this layer's table and lengths;
- * scale: softmax scale (finite). workspace: device memory of at least
+ * scale: softmax scale; scale and scale * log2(e) must be finite in FP32
+ * (else PA_ERR_INVALID), and scale * <q, k> * log2(e) must stay finite in
+ * FP32 for every attended key (a precondition on device data). workspace:
+ * device memory of at least
  * pa_decode_workspace_bytes(...) bytes (may be NULL when that is 0); its
  * contents need no initialisation and are overwritten. Queued on `stream`.
  * num_seqs == 0 queues nothing.

@@ -164,6 +164,46 @@ def _need(t, name, dtypes, ndim=None):
         raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
 
 
+def _shape(t, name, expected):
+    if tuple(t.shape) != tuple(expected):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(expected)}")
+
+
+def _same_device(pool, *tensors):
+    dev = pool.k_pages.device
+    for t in tensors:
+        if t is not None and t.device != dev:
+            raise ValueError(f"tensor on {t.device}, pool on {dev}")
+
+
+def _check_decode_args(pool, q, block_tables, context_lens, out):
+    """Shapes of a decode call against the pool and the batch: q ``[B][Hq][d]``
+    with d the pool's head_dim and Hq a multiple of its KV heads, one block
+    table row and one context length per sequence, out ``[B][Hq][d]``."""
+    num_seqs, num_q_heads, d = q.shape
+    if d != pool.head_dim:
+        raise ValueError(f"q head_dim {d} != pool head_dim {pool.head_dim}")
+    if num_q_heads % pool.num_kv_heads != 0:
+        raise ValueError(f"{num_q_heads} query heads are not a multiple of {pool.num_kv_heads} KV heads")
+    if block_tables.shape[0] != num_seqs:
+        raise ValueError(f"block_tables has {block_tables.shape[0]} rows for {num_seqs} sequences")
+    if context_lens.numel() != num_seqs:
+        raise ValueError(f"context_lens has {context_lens.numel()} values for {num_seqs} sequences")
+    if out is not None:
+        _shape(out, "out", (num_seqs, num_q_heads, d))
+    _same_device(pool, q, block_tables, context_lens, out)
+
+
+def _check_new_rows(pool, num_seqs, k_new, v_new, positions):
+    """k_new / v_new ``[B][Hkv][d]`` and one position per sequence."""
+    want = (num_seqs, pool.num_kv_heads, pool.head_dim)
+    _shape(k_new, "k_new", want)
+    _shape(v_new, "v_new", want)
+    if positions.numel() != num_seqs:
+        raise ValueError(f"positions has {positions.numel()} values for {num_seqs} sequences")
+    _same_device(pool, k_new, v_new, positions)
+
+
 def _bf16_types():
     import torch
     return (torch.bfloat16, torch.int16)
@@ -217,6 +257,8 @@ def kv_append(pool: Pool, k_new, v_new, block_tables, positions, stream=None):
     _need(block_tables, "block_tables", (torch.int32,), 2)
     _need(positions, "positions", (torch.int32,), 1)
     num_seqs = block_tables.shape[0]
+    _check_new_rows(pool, num_seqs, k_new, v_new, positions)
+    _same_device(pool, block_tables)
     _check(lib().pa_kv_append(pool.handle, _ptr(k_new), _ptr(v_new), num_seqs, _ptr(block_tables),
                               block_tables.shape[1], _ptr(positions), _stream(stream)),
            "pa_kv_append")
@@ -229,6 +271,7 @@ def decode(pool: Pool, q, block_tables, context_lens, scale: float, out=None, wo
     _need(q, "q", _bf16_types(), 3)
     _need(block_tables, "block_tables", (torch.int32,), 2)
     _need(context_lens, "context_lens", (torch.int32,), 1)
+    _check_decode_args(pool, q, block_tables, context_lens, out)
     num_seqs, num_q_heads, d = q.shape
     stride = block_tables.shape[1]
     if out is None:
@@ -293,6 +336,8 @@ def decode_planned(pool: Pool, q, block_tables, context_lens, scale: float, plan
     _need(block_tables, "block_tables", (torch.int32,), 2)
     _need(context_lens, "context_lens", (torch.int32,), 1)
     _need(plan, "plan", (torch.int32,), 1)
+    _check_decode_args(pool, q, block_tables, context_lens, out)
+    _same_device(pool, plan)
     num_seqs, num_q_heads, d = q.shape
     stride = block_tables.shape[1]
     if out is None:
@@ -320,6 +365,21 @@ def _chunk_common(q_or_k, query_start, block_tables, context_lens, max_chunk):
     return num_seqs, q_or_k.shape[0], block_tables.shape[1], int(max_chunk)
 
 
+def _check_chunk_rows(pool, num_rows, k_rows, v_rows, q=None, out=None, *others):
+    """Chunk rows: k_rows / v_rows ``[N][Hkv][d]``, q and out ``[N][Hq][d]`` with
+    Hq a multiple of the pool's KV heads and d its head_dim."""
+    want = (num_rows, pool.num_kv_heads, pool.head_dim)
+    _shape(k_rows, "k_rows", want)
+    _shape(v_rows, "v_rows", want)
+    if q is not None:
+        if q.shape[2] != pool.head_dim or q.shape[1] % pool.num_kv_heads != 0:
+            raise ValueError(f"q shape {tuple(q.shape)} does not fit the pool "
+                             f"({pool.num_kv_heads} KV heads, head_dim {pool.head_dim})")
+        if out is not None:
+            _shape(out, "out", tuple(q.shape))
+    _same_device(pool, k_rows, v_rows, q, out, *others)
+
+
 def kv_write(pool: Pool, k_rows, v_rows, query_start, block_tables, context_lens, max_chunk: int,
              stream=None):
     """Write chunks of new tokens' K/V (``[N][Hkv][d]``) into their pages (pa_kv_write)."""
@@ -327,6 +387,7 @@ def kv_write(pool: Pool, k_rows, v_rows, query_start, block_tables, context_lens
     _need(v_rows, "v_rows", _bf16_types(), 3)
     num_seqs, num_rows, stride, max_chunk = _chunk_common(k_rows, query_start, block_tables,
                                                           context_lens, max_chunk)
+    _check_chunk_rows(pool, num_rows, k_rows, v_rows, None, None, query_start, block_tables, context_lens)
     _check(lib().pa_kv_write(pool.handle, _ptr(k_rows), _ptr(v_rows), num_seqs, num_rows, max_chunk,
                              _ptr(query_start), _ptr(block_tables), stride, _ptr(context_lens),
                              _stream(stream)), "pa_kv_write")
@@ -342,9 +403,11 @@ def prefill(pool: Pool, q, k_rows, v_rows, query_start, block_tables, context_le
     _need(v_rows, "v_rows", _bf16_types(), 3)
     num_seqs, num_rows, stride, max_chunk = _chunk_common(q, query_start, block_tables, context_lens,
                                                           max_chunk)
+    if out is not None:
+        _need(out, "out", (torch.float32,), 3)
+    _check_chunk_rows(pool, num_rows, k_rows, v_rows, q, out, query_start, block_tables, context_lens)
     if out is None:
         out = torch.empty(tuple(q.shape), dtype=torch.float32, device=q.device)
-    _need(out, "out", (torch.float32,), 3)
     _check(lib().pa_prefill(pool.handle, _ptr(q), _ptr(k_rows), _ptr(v_rows), num_seqs, q.shape[1],
                             num_rows, max_chunk, _ptr(query_start), _ptr(block_tables), stride,
                             _ptr(context_lens), float(scale), _ptr(out), _stream(stream)),
@@ -417,9 +480,11 @@ def prefill_planned(pool: Pool, q, k_rows, v_rows, query_start, block_tables, co
     _need(plan, "plan", (torch.int32,), 1)
     num_seqs, num_rows, stride, max_chunk = _chunk_common(q, query_start, block_tables, context_lens,
                                                           max_chunk)
+    if out is not None:
+        _need(out, "out", (torch.float32,), 3)
+    _check_chunk_rows(pool, num_rows, k_rows, v_rows, q, out, query_start, block_tables, context_lens)
     if out is None:
         out = torch.empty(tuple(q.shape), dtype=torch.float32, device=q.device)
-    _need(out, "out", (torch.float32,), 3)
     _check(lib().pa_prefill_planned(pool.handle, _ptr(q), _ptr(k_rows), _ptr(v_rows), num_seqs, q.shape[1],
                                     num_rows, max_chunk, _ptr(query_start), _ptr(block_tables), stride,
                                     _ptr(context_lens), float(scale), _ptr(out), _ptr(plan), plan.numel(),
@@ -437,6 +502,8 @@ def decode_append(pool: Pool, q, k_new, v_new, positions, block_tables, context_
     _need(positions, "positions", (torch.int32,), 1)
     _need(block_tables, "block_tables", (torch.int32,), 2)
     _need(context_lens, "context_lens", (torch.int32,), 1)
+    _check_decode_args(pool, q, block_tables, context_lens, out)
+    _check_new_rows(pool, q.shape[0], k_new, v_new, positions)
     num_seqs, num_q_heads, d = q.shape
     stride = block_tables.shape[1]
     if out is None:

@@ -48,6 +48,11 @@ constexpr int kDeviceCUs = 256;
 constexpr int kCUsPerXCD = 32;
 constexpr int64_t kPlanMaxSplits = 1 << 11; // and the split in the 11 above them
 
+// The kernels work with scores in log2 units: scale * log2(e) must be a
+// finite FP32 value.
+float scale_log2_of(float scale) { return static_cast<float>(static_cast<double>(scale) * 1.4426950408889634); }
+bool scale_ok(float scale) { return std::isfinite(scale) && std::isfinite(scale_log2_of(scale)); }
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
@@ -262,7 +267,7 @@ static pa_status decode_impl(const pa_pool* pool, const void* q, bool fused, con
   if (!pool) return PA_ERR_NULL;
   if (num_seqs < 0 || num_q_heads < 1 || max_pages_per_seq < 1) return PA_ERR_INVALID;
   if (static_cast<int64_t>(max_pages_per_seq) * pakv::kPage > INT_MAX) return PA_ERR_INVALID;
-  if (!std::isfinite(scale)) return PA_ERR_INVALID;
+  if (!scale_ok(scale)) return PA_ERR_INVALID;
   if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_INVALID;
   const int group = num_q_heads / pool->num_kv_heads;
   if (group > kMaxGroup) return PA_ERR_UNSUPPORTED;
@@ -304,7 +309,7 @@ static pa_status decode_impl(const pa_pool* pool, const void* q, bool fused, con
   a.group = group;
   a.stride = max_pages_per_seq;
   a.s_max = static_cast<int32_t>(splits_for(d, max_pages_per_seq));
-  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  a.scale_log2 = scale_log2_of(scale);
   a.k_new = fused ? static_cast<const uint16_t*>(k_new) : nullptr;
   a.v_new = fused ? static_cast<const uint16_t*>(v_new) : nullptr;
   a.positions = fused ? positions : nullptr;
@@ -504,7 +509,7 @@ static pa_status prefill_impl(const pa_pool* pool, const void* q, const void* k_
                                   max_pages_per_seq, context_lens);
   if (st != PA_OK) return st;
   if (num_q_heads < 1 || num_q_heads % pool->num_kv_heads != 0) return PA_ERR_INVALID;
-  if (!std::isfinite(scale)) return PA_ERR_INVALID;
+  if (!scale_ok(scale)) return PA_ERR_INVALID;
   const int group = num_q_heads / pool->num_kv_heads;
   if (group > kMaxGroup) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0 || num_rows == 0 || max_chunk == 0) return PA_OK;
@@ -541,7 +546,7 @@ static pa_status prefill_impl(const pa_pool* pool, const void* q, const void* k_
   a.stride = max_pages_per_seq;
   a.max_chunk = max_chunk;
   a.row_blocks = static_cast<int32_t>(row_blocks);
-  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  a.scale_log2 = scale_log2_of(scale);
   a.plan = plan;
   (void)hipGetLastError();
   {

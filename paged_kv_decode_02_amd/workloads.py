@@ -98,9 +98,31 @@ def normal_table_bits(sigma: float) -> np.ndarray:
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
+def _mix32_u32(x: np.ndarray) -> np.ndarray:
+    """_mix32 on a uint32 numpy array, in place: uint32 products wrap modulo
+    2^32 by themselves, which is the arithmetic the hash is defined with."""
+    x ^= x >> np.uint32(16)
+    x *= np.uint32(_C1)
+    x ^= x >> np.uint32(15)
+    x *= np.uint32(_C2)
+    x ^= x >> np.uint32(16)
+    return x
+
+
+def hash32_np(seed: int, stream: int, idx: np.ndarray) -> np.ndarray:
+    """hash32 of non-negative int64 indices with uint32 numpy arithmetic (the
+    same function; faster on the host than the int64 form torch needs)."""
+    idx = np.asarray(idx, dtype=np.int64)
+    key = np.uint32(stream_key(seed, stream))
+    inner = _mix32_u32((idx >> 32).astype(np.uint32) ^ key)
+    lo = idx.astype(np.uint32)
+    lo ^= inner
+    return _mix32_u32(lo)
+
+
 def values_np(seed: int, stream: int, idx: np.ndarray, table: np.ndarray) -> np.ndarray:
-    h = hash32(seed, stream, np.asarray(idx, dtype=np.int64))
-    return table[(h >> 16).astype(np.int64)]
+    h = hash32_np(seed, stream, idx)
+    return table[h >> np.uint32(16)]
 
 
 # ------------------------------------------------------------------ workload

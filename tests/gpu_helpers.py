@@ -98,6 +98,22 @@ class Uploaded:
         return self.out
 
 
+def full_oracle(w, up):
+    """Oracle output of every layer and sequence of a (small) workload: per
+    layer, the oracle's own append first when the workload appends."""
+    k = w.pool_bits("k")
+    v = w.pool_bits("v")
+    outs = []
+    for layer in range(w.num_layers):
+        kk, vv = k, v
+        if w.append:
+            kk, vv = oracle.kv_append(k, v, up.k_new_host[layer], up.v_new_host[layer],
+                                      w.block_tables[layer], w.positions)
+        outs.append(oracle.decode_attention(up.q_host[layer], kk, vv, w.block_tables[layer],
+                                            w.ctx_lens, w.scale))
+    return np.stack(outs)
+
+
 def oracle_rows(w, layer, seqs, q_host, k_new_host=None, v_new_host=None):
     """Oracle outputs for the listed sequences of one layer, from host-regenerated
     pages (only the pages those sequences reference)."""

@@ -2,10 +2,12 @@
 same seeded BF16 inputs.
 
 * Tiny, C2 and C3 workloads: every output element.
-* C5 (64 x up to 16K tokens, 28q/4kv, d=128) and C4 (16 layers x 256 seqs,
-  append then decode): launched at full size exactly as the benchmark does,
-  checked on sampled sequences the oracle computes one by one (including the
-  longest and shortest contexts).
+* C5 (64 x up to 16K tokens, 28q/4kv, d=128): launched at full size exactly
+  as the benchmark does; every output of all 64 sequences.
+* C4 (16 layers x 256 seqs, append then decode): the benchmark's step at full
+  size; every output of all 256 sequences in layers 0, 7 and 15, sampled
+  sequences in other layers, and the appended pages bit for bit. The oracle
+  runs in host worker processes on host-regenerated pages.
 * Edge cases on small custom workloads: empty contexts, one token, page and
   split boundaries, ragged tails, group sizes 1..16, one KV head, contexts
   filling the whole block table.
@@ -17,25 +19,12 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import Uploaded, check_parity, device, log, oracle_rows
+from gpu_helpers import Uploaded, check_parity, device, full_oracle, log, oracle_rows
+from oracle_units import host_workers, oracle_units
 from paged_kv_decode_02_amd import binding as B
 from paged_kv_decode_02_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
-
-
-def full_oracle(w, up):
-    k = w.pool_bits("k")
-    v = w.pool_bits("v")
-    outs = []
-    for layer in range(w.num_layers):
-        kk, vv = k, v
-        if w.append:
-            kk, vv = oracle.kv_append(k, v, up.k_new_host[layer], up.v_new_host[layer],
-                                      w.block_tables[layer], w.positions)
-        outs.append(oracle.decode_attention(up.q_host[layer], kk, vv, w.block_tables[layer],
-                                            w.ctx_lens, w.scale))
-    return np.stack(outs)
 
 
 @pytest.mark.parametrize("name", ["tiny", "c2", "c3"])
@@ -53,31 +42,39 @@ def test_named_workload_all_outputs(name):
     log(f"{name}: max abs {a:.2e} max rel {r:.2e}")
 
 
-def _sample(w, k=8):
-    order = np.argsort(w.ctx_lens, kind="stable")
-    picks = {int(order[0]), int(order[-1]), int(order[len(order) // 2])}
-    rng = np.random.default_rng(7)
-    picks.update(int(x) for x in rng.choice(w.num_seqs, size=k, replace=False))
-    return sorted(picks)
-
-
-def test_c5_full_launch_sampled():
+def test_c5_full_launch_all_outputs():
+    """C5 launched at full size as the benchmark launches it (plan, split
+    kernel, merge); every output of the 64 sequences against the oracle,
+    computed on the host cores from host-regenerated pages."""
+    import torch
     dev = device()
     w = W.make_workload("c5")
-    log(f"c5: B=64 Hq=28 Hkv=4 d=128 pages={w.num_pages} max_ctx={w.ctx_lens.max()} entry=pa_decode")
+    log(f"c5: B=64 Hq=28 Hkv=4 d=128 pages={w.num_pages} max_ctx={w.ctx_lens.max()} "
+        f"entry=pa_decode_planned, oracle on {host_workers()} host workers")
     up = Uploaded(w, dev)
-    out = up.step().cpu().numpy()
-    seqs = _sample(w)
-    ref = oracle_rows(w, 0, seqs, up.q_host)
-    a, r = check_parity(out[0, seqs], ref, "c5 sampled")
-    log(f"c5 sampled {seqs}: max abs {a:.2e} max rel {r:.2e}")
+    out = up.step(planned=True).cpu().numpy()
+    torch.cuda.synchronize()
+    plain = up.step().cpu().numpy()
+    assert np.array_equal(plain, out), "c5: planned != plain"
+    ref = oracle_units("c5", [(0, b) for b in range(w.num_seqs)])
+    full = np.stack([ref[(0, b)] for b in range(w.num_seqs)])
+    a, r = check_parity(out[0], full, "c5 all sequences")
+    log(f"c5 all 64 sequences: max abs {a:.2e} max rel {r:.2e}")
 
 
-def test_c4_full_step_sampled():
+C4_LAYERS = (0, 7, 15)
+
+
+def test_c4_full_step_all_sequences():
+    """The C4 step exactly as the benchmark runs it (plan, then per layer
+    pa_kv_append and pa_decode_planned), at full size. Layers 0, 7 and 15:
+    every output of all 256 sequences against the oracle (which applies its
+    own append first). Sampled units: the appended page bit for bit."""
     import torch
     dev = device()
     w = W.make_workload("c4")
-    log(f"c4: L=16 B=256 pages={w.num_pages} max_ctx={w.ctx_lens.max()} entry=pa_kv_append+pa_decode_planned")
+    log(f"c4: L=16 B=256 pages={w.num_pages} max_ctx={w.ctx_lens.max()} "
+        f"entry=pa_kv_append+pa_decode_planned, oracle on {host_workers()} host workers")
     up = Uploaded(w, dev)
     out = up.step(fused=False, planned=True).cpu().numpy()   # the step the benchmark times
     torch.cuda.synchronize()
@@ -85,13 +82,16 @@ def test_c4_full_step_sampled():
     for layer in (0, 15):
         plain = B.decode(up.pool, up.q[layer], up.bt[layer], up.ctx, float(w.scale), workspace=up.workspace)
         assert np.array_equal(plain.cpu().numpy(), out[layer]), f"c4 layer {layer}: planned != plain"
+    ref = oracle_units("c4", [(l, b) for l in C4_LAYERS for b in range(w.num_seqs)])
+    for layer in C4_LAYERS:
+        full = np.stack([ref[(layer, b)] for b in range(w.num_seqs)])
+        a, r = check_parity(out[layer], full, f"c4 layer {layer} all sequences")
+        log(f"c4 layer {layer}, all 256 sequences: max abs {a:.2e} max rel {r:.2e}")
     rng = np.random.default_rng(3)
     order = np.argsort(w.ctx_lens, kind="stable")
     cases = [(0, int(order[-1])), (15, int(order[0])), (7, int(order[128]))]
     cases += [(int(rng.integers(16)), int(rng.integers(256))) for _ in range(6)]
     for layer, b in cases:
-        ref = oracle_rows(w, layer, [b], up.q_host, up.k_new_host, up.v_new_host)
-        a, r = check_parity(out[layer, [b]], ref, f"c4 layer {layer} seq {b}")
         # the appended slot, and the rest of its page, bit for bit
         n = int(w.ctx_lens[b])
         page = int(w.block_tables[layer, b, (n - 1) // 16])
@@ -102,7 +102,13 @@ def test_c4_full_step_sampled():
         got_v = up.v_pool[page].cpu().numpy().view(np.uint16)
         assert np.array_equal(got_k, exp_k[0]), f"c4 append K page {page}"
         assert np.array_equal(got_v, exp_v[0]), f"c4 append V page {page}"
-        log(f"c4 layer {layer} seq {b} ctx {n}: max abs {a:.2e} max rel {r:.2e}")
+    # the other layers: sampled units
+    for layer, b in cases:
+        if layer in C4_LAYERS:
+            continue
+        one = oracle_rows(w, layer, [b], up.q_host, up.k_new_host, up.v_new_host)
+        a, r = check_parity(out[layer, [b]], one, f"c4 layer {layer} seq {b}")
+        log(f"c4 layer {layer} seq {b}: max abs {a:.2e} max rel {r:.2e}")
 
 
 EDGE_CASES = [

@@ -205,9 +205,74 @@ def test_error_paths_on_gpu():
     with pytest.raises(B.PakvError) as e:
         B.decode(up.pool, up.q[0], up.bt[0], up.ctx, 0.125, workspace=small)
     assert e.value.status == 5
-    with pytest.raises(B.PakvError) as e:
-        B.decode(up.pool, up.q[0][:, :12].contiguous(), up.bt[0], up.ctx, 0.125)
-    assert e.value.status == 2
+    # the C ABI itself refuses a query-head count that is not a multiple of the KV heads
+    q12 = up.q[0][:, :12].contiguous()
+    st = B.lib().pa_decode(up.pool.handle, q12.data_ptr(), 2, 12, up.bt[0].data_ptr(), w.stride,
+                           up.ctx.data_ptr(), 0.125, up.out[0].data_ptr(), up.workspace.data_ptr(),
+                           up.workspace.numel(), None)
+    assert st == 2
+    # and a scale whose log2(e) multiple is not finite in FP32
+    st = B.lib().pa_decode(up.pool.handle, up.q[0].data_ptr(), 2, 32, up.bt[0].data_ptr(), w.stride,
+                           up.ctx.data_ptr(), 3.0e38, up.out[0].data_ptr(), up.workspace.data_ptr(),
+                           up.workspace.numel(), None)
+    assert st == 2
+
+
+def test_binding_rejects_mismatched_shapes():
+    """Every tensor is checked against the pool and the batch before anything
+    is queued: a wrong shape raises ValueError and leaves the pool and the
+    output untouched."""
+    import torch
+    dev = device()
+    w = W.custom(seed=16, ctx_lens=[300, 40, 9], append=True)
+    up = Uploaded(w, dev)
+    log("binding shape checks")
+    q, bt, ctx, kn, vn, pos = up.q[0], up.bt[0], up.ctx, up.k_new[0], up.v_new[0], up.pos
+    out = torch.full((3, 32, 64), 7.0, device=dev)
+    k0, v0 = up.k_pool.clone(), up.v_pool.clone()
+    bad_decode = [
+        dict(q=q[:2].contiguous()),                                   # 2 queries, 3 table rows
+        dict(bt=bt[:2].contiguous()),                                 # 2 table rows
+        dict(ctx=ctx[:2].contiguous()),                               # 2 context lengths
+        dict(out=torch.empty((3, 32, 32), device=dev)),               # wrong output shape
+        dict(q=torch.zeros((3, 32, 128), dtype=torch.int16, device=dev)),   # head_dim 128 on a d=64 pool
+        dict(q=torch.zeros((3, 12, 64), dtype=torch.int16, device=dev)),    # 12 heads over 8 KV heads
+    ]
+    for bad in bad_decode:
+        args = dict(q=q, bt=bt, ctx=ctx, out=out)
+        args.update(bad)
+        with pytest.raises(ValueError):
+            B.decode(up.pool, args["q"], args["bt"], args["ctx"], 0.125, out=args["out"])
+        plan = torch.from_numpy(B.decode_plan(up.pool, w.ctx_lens, w.stride)).to(dev)
+        with pytest.raises(ValueError):
+            B.decode_planned(up.pool, args["q"], args["bt"], args["ctx"], 0.125, plan, out=args["out"])
+    bad_rows = [
+        dict(kn=kn[:2].contiguous()),
+        dict(vn=torch.zeros((3, 8, 32), dtype=torch.int16, device=dev)),
+        dict(pos=pos[:1].contiguous()),
+        dict(kn=torch.zeros((3, 4, 64), dtype=torch.int16, device=dev)),
+    ]
+    for bad in bad_rows:
+        args = dict(kn=kn, vn=vn, pos=pos)
+        args.update(bad)
+        with pytest.raises(ValueError):
+            B.kv_append(up.pool, args["kn"], args["vn"], bt, args["pos"])
+        with pytest.raises(ValueError):
+            B.decode_append(up.pool, q, args["kn"], args["vn"], args["pos"], bt, ctx, 0.125, out=out)
+    # chunk rows for prefill / chunk write
+    qs = torch.tensor([0, 2, 3, 3], dtype=torch.int32, device=dev)
+    rows_k = torch.zeros((3, 8, 64), dtype=torch.int16, device=dev)
+    with pytest.raises(ValueError):
+        B.kv_write(up.pool, rows_k[:2].contiguous(), rows_k, qs, bt, ctx, 2)
+    with pytest.raises(ValueError):
+        B.prefill(up.pool, torch.zeros((3, 32, 64), dtype=torch.int16, device=dev), rows_k,
+                  torch.zeros((3, 8, 128), dtype=torch.int16, device=dev), qs, bt, ctx, 0.125, 2)
+    with pytest.raises(ValueError):
+        B.prefill(up.pool, torch.zeros((3, 32, 64), dtype=torch.int16, device=dev), rows_k, rows_k,
+                  qs, bt, ctx, 0.125, 2, out=torch.empty((3, 32, 32), device=dev))
+    torch.cuda.synchronize()
+    assert bool((up.k_pool == k0).all()) and bool((up.v_pool == v0).all())
+    assert bool((out == 7.0).all())
 
 
 def test_stream_read_helper():

@@ -21,6 +21,16 @@ def test_hash_matches_python_ints():
         assert g == ref
 
 
+def test_uint32_host_hash_matches_int64_form():
+    rng = np.random.default_rng(11)
+    idx = np.concatenate([np.arange(5000, dtype=np.int64),
+                          rng.integers(0, 1 << 40, 20000, dtype=np.int64),
+                          np.array([(1 << 32) - 1, 1 << 32, (1 << 33) + 7], np.int64)])
+    for seed, stream in [(7, 3), (1004, 1), (1005, 5)]:
+        assert np.array_equal(W.hash32_np(seed, stream, idx).astype(np.int64),
+                              W.hash32(seed, stream, idx))
+
+
 def test_torch_and_numpy_generators_agree():
     import torch
     w = W.custom(5, [1, 17, 40, 3], num_q_heads=8, num_kv_heads=2, head_dim=64)
