@@ -4,15 +4,17 @@
 
 A step is one pass of the whole path over one batch: for the default workload
 (16 layers, 256 sequences, lognormal contexts, 32q/8kv, d=64) that is the
-launch plan made on the host and copied to the device, then per layer the
-paged append of the new token's K/V and paged decode attention (split kernel
-+ merge kernel), launched from Python (--graph replays them from a HIP graph
-captured once per input replica instead). Inputs are resident in HBM before
-timing. Prints one JSON line: achieved KV-read GB/s over the timed steps, the
-roofline of the dominant kernel (the decode split kernel, timed with HIP
-events on the launch stream in a second, eager pass over the same steps),
-and a CPU baseline (the FP64 oracle on a bounded sample of the same workload,
-on the host cores).
+launch plan made on the host from the host's context lengths, then per layer
+the paged append of the new token's K/V and paged decode attention, the plan
+carried in the decode kernel's arguments (pa_decode_planned_host), launched
+from Python through calls prepared once (--graph replays each step's launches
+from a HIP graph captured once per input replica instead, with the plan in
+device memory). Inputs are resident in HBM before timing. Prints one JSON
+line: achieved KV-read GB/s over the timed steps, the roofline of the dominant
+kernel (the decode kernel, timed with HIP events on the launch stream in a
+separate pass over the same steps), the same figures for the other decode
+configurations (tiny, c2, c3, c5) under "configs", and a CPU baseline (the
+FP64 oracle on a bounded sample of the same workload, on the host cores).
 """
 
 from __future__ import annotations
@@ -31,7 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E peak
 MALL_BYTES = 256 << 20   # device last-level (Infinity) cache
-PROFILE = os.path.join(ROOT, "profiles", "decode_split_kernel_c4.md")
+PROFILE = os.path.join(ROOT, "profiles", "decode_kernel_c4.md")
 PREFILL_PROFILE = os.path.join(ROOT, "profiles", "prefill_kernel_prefill.md")
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense BF16 matrix-core peak
 KERNEL_SOURCES = ("paged_kv_decode_02_amd/csrc/pakv_kernels.h", "paged_kv_decode_02_amd/csrc/pakv.hip")
@@ -68,6 +70,8 @@ def parse():
                     help="budget of timed oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="measure only --workload (default: also every other decode configuration)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step's launches from a HIP graph captured once per replica "
                          "(default: launch from Python; measured faster on this stack)")
@@ -75,9 +79,10 @@ def parse():
 
 
 class Inputs:
-    """One replica of a workload's device inputs."""
+    """One replica of a workload's device inputs, with the step's launches
+    prepared once (arguments checked and marshalled) and a host plan buffer."""
 
-    def __init__(self, w, dev, B):
+    def __init__(self, w, dev, B, stream):
         import torch
         self.k = w.pool_device("k", dev)
         self.v = w.pool_device("v", dev)
@@ -89,79 +94,92 @@ class Inputs:
             self.k_new = torch.from_numpy(w.new_kv_bits("k").view(np.int16)).to(dev)
             self.v_new = torch.from_numpy(w.new_kv_bits("v").view(np.int16)).to(dev)
             self.pos = torch.from_numpy(w.positions).to(dev)
-        # launch plan: made on the host from the host copy of the context
-        # lengths once per step (every layer shares it), copied to the device
-        # from pinned memory; two host buffers so that the plan of the next
-        # step is never written while the previous copy may still read it
-        self.ctx_host = w.ctx_lens.copy()
-        cap = B.decode_plan_capacity(self.pool, w.num_seqs, w.stride)
-        self.plan_pin = [torch.empty(cap, dtype=torch.int32, pin_memory=True) for _ in range(2)]
-        self.plan_copied = [None, None]
-        self.plan_dev = torch.empty(cap, dtype=torch.int32, device=dev)
-        self.step_no = 0
-        self.graph = None
-        self.graph_items = -1
         need = B.decode_workspace_bytes(self.pool, w.num_seqs, w.num_q_heads, w.stride)
         self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
         self.out = torch.empty((w.num_layers, w.num_seqs, w.num_q_heads, w.head_dim),
                                dtype=torch.float32, device=dev)
+        # launch plan: made on the host from the host copy of the context
+        # lengths once per step (every layer shares it); a small plan travels
+        # in each decode launch's arguments, a larger one is copied to the
+        # device once per step
+        self.ctx_host = np.ascontiguousarray(w.ctx_lens, dtype=np.int32).copy()
+        self.plan = B.HostPlan(self.pool, self.ctx_host, w.num_q_heads, w.stride)
+        if self.plan.make() > B.INLINE_PLAN_WORDS:
+            self.plan = B.DevicePlan(self.pool, self.ctx_host, w.num_q_heads, w.stride, dev)
+        self.decode = [B.PreparedDecode(self.pool, self.q[l], self.bt[l], self.ctx, float(w.scale), self.plan,
+                                        self.out[l], workspace=self.ws, stream=stream)
+                       for l in range(w.num_layers)]
+        self.append = ([B.PreparedAppend(self.pool, self.k_new[l], self.v_new[l], self.bt[l], self.pos,
+                                         stream=stream) for l in range(w.num_layers)] if w.append else [])
+        # --graph: the plan in device memory, copied from pinned host memory
+        self.graph = None
+        self.graph_words = -1
+        self.plan_dev = None
+
+
+def run_step(w, x, B, stream):
+    """One step: the launch plan (host), then per layer the paged append of the
+    new token's K/V (pa_kv_append) and paged decode attention with the plan in
+    the kernel's arguments (pa_decode_planned_host). Replayed from a HIP graph
+    instead when one was captured for this replica."""
+    import torch
+    if x.graph is not None:
+        words = upload_plan(w, x, B, stream)
+        if words == x.graph_words:
+            with torch.cuda.stream(stream):
+                x.graph.replay()
+            return
+    if isinstance(x.plan, B.DevicePlan):
+        x.plan.upload(stream)
+    else:
+        x.plan.make()
+    for layer in range(w.num_layers):
+        if w.append:
+            x.append[layer]()
+        x.decode[layer]()
 
 
 def upload_plan(w, x, B, stream):
-    """The launch plan for this step's context lengths: made on the host into a
-    pinned buffer, copied to the device on the launch stream. Returns the
-    device view the decode launches read."""
+    """--graph: this step's plan made on the host into a pinned buffer and
+    copied on the launch stream into the device buffer the captured launches
+    read (two pinned buffers, so a plan is never rewritten while its copy may
+    still be pending). Returns its length in words."""
     import torch
+    hp = x.plan.host if isinstance(x.plan, B.DevicePlan) else x.plan
+    words = hp.make()
     k = x.step_no & 1
     x.step_no += 1
     if x.plan_copied[k] is not None:
         x.plan_copied[k].synchronize()
-    n = B.decode_plan_into(x.pool, x.ctx_host, w.stride, x.plan_pin[k])
-    plan = x.plan_dev[:n]
+    x.plan_pin[k][:words].copy_(torch.from_numpy(hp.buf[:words]))
     with torch.cuda.stream(stream):
-        plan.copy_(x.plan_pin[k][:n], non_blocking=True)
+        x.plan_dev[:words].copy_(x.plan_pin[k][:words], non_blocking=True)
         ev = torch.cuda.Event()
         ev.record(stream)
         x.plan_copied[k] = ev
-    return plan
-
-
-def run_layers(w, x, B, stream, plan):
-    """Per layer: the paged append of the new token's K/V (pa_kv_append), then
-    paged decode attention driven by the plan (pa_decode_planned,
-    bit-identical to pa_decode). The single-launch pa_decode_append gives
-    bit-identical results but measures slower, so the step uses the two calls."""
-    for layer in range(w.num_layers):
-        if w.append:
-            B.kv_append(x.pool, x.k_new[layer], x.v_new[layer], x.bt[layer], x.pos, stream=stream)
-        B.decode_planned(x.pool, x.q[layer], x.bt[layer], x.ctx, float(w.scale), plan,
-                         out=x.out[layer], workspace=x.ws, stream=stream)
-
-
-def run_step(w, x, B, stream):
-    """One step: the launch plan, then every layer's launches (replayed from a
-    HIP graph when one was captured for this replica)."""
-    import torch
-    plan = upload_plan(w, x, B, stream)
-    if x.graph is not None and plan.numel() == x.graph_items:
-        with torch.cuda.stream(stream):
-            x.graph.replay()
-    else:
-        run_layers(w, x, B, stream, plan)
+    return words
 
 
 def capture_step(w, x, B, stream):
-    """Capture one step's launches (all layers, no plan upload) into a HIP graph
-    through torch; the plan buffer is read at replay time, so a replay serves
-    any plan with the same number of items."""
+    """Capture one step's launches (all layers, the plan in device memory) into
+    a HIP graph through torch; a replay serves any plan of the same length."""
     import torch
-    plan = upload_plan(w, x, B, stream)
+    hp = x.plan.host if isinstance(x.plan, B.DevicePlan) else x.plan
+    x.plan_pin = [torch.empty(hp.cap, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    x.plan_copied = [None, None]
+    x.step_no = 0
+    x.plan_dev = torch.empty(hp.cap, dtype=torch.int32, device=stream.device)
+    words = upload_plan(w, x, B, stream)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
-        run_layers(w, x, B, stream, plan)
+        for layer in range(w.num_layers):
+            if w.append:
+                B.kv_append(x.pool, x.k_new[layer], x.v_new[layer], x.bt[layer], x.pos, stream=stream)
+            B.decode_planned(x.pool, x.q[layer], x.bt[layer], x.ctx, float(w.scale), x.plan_dev[:words],
+                             out=x.out[layer], workspace=x.ws, stream=stream)
     torch.cuda.synchronize()
-    x.graph, x.graph_items = g, plan.numel()
+    x.graph, x.graph_words = g, words
 
 
 def step_percentiles(run_one, steps, stream):
@@ -226,6 +244,14 @@ def stream_ceiling(B, dev, stream):
     return rates[-1], rates[len(rates) // 2]
 
 
+def host_cores() -> int:
+    """Cores this process may run on (the box's share of the host)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(w, budget_s):
     """The FP64 oracle on (layer, sequence) units of the same workload until about
     budget_s seconds of oracle time have run. Page regeneration is not timed."""
@@ -264,7 +290,7 @@ def cpu_baseline(w, budget_s):
     if limiter is not None:
         limiter.unregister() if hasattr(limiter, "unregister") else None
     gbps = nbytes / t_oracle / 1e9
-    return {"value": round(gbps, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(gbps, 6), "unit": "GB/s", "cores": 1, "host_cores": host_cores(), "kind": "oracle",
             "sample": f"{done} of {len(units)} (layer, sequence) units, random order, "
                       f"{nbytes / 1e6:.1f} MB of KV in {t_oracle:.1f} s of oracle time; "
                       f"BLAS limited to 1 thread",
@@ -377,7 +403,8 @@ def prefill_cpu_baseline(w, budget_s):
         t_oracle += time.perf_counter() - t0
     if limiter is not None and hasattr(limiter, "unregister"):
         limiter.unregister()
-    return {"value": round(flops / t_oracle / 1e12, 9), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+    return {"value": round(flops / t_oracle / 1e12, 9), "unit": "TFLOP/s", "cores": 1, "host_cores": host_cores(),
+            "kind": "oracle",
             "sample": f"{rows_done} random chunk rows (all query heads each) of random (layer, sequence) "
                       f"units, {flops / 1e9:.2f} GFLOP in {t_oracle:.1f} s of oracle time (gather "
                       f"included); BLAS limited to 1 thread"}
@@ -485,6 +512,120 @@ def prefill_main(args):
     print(json.dumps(result), flush=True)
 
 
+DECODE_NAMES = {
+    "tiny": "tiny: 1 seq x ctx 128, 32q/8kv d64, 1 layer",
+    "c2": "batch 8, ctx U[1,512], 32q/8kv d64, 1 layer",
+    "c3": "batch 64, ctx U[256,2048], 32q/8kv d64, 1 layer",
+    "c4": "full decode step: 16 layers x (append + decode), batch 256, ctx lognormal median 1024 "
+          "clipped [16,8192], 32q/8kv d64",
+    "c5": "batch 64, ctx U[4096,16384], 28q/4kv d128, 1 layer",
+}
+
+
+def measure_decode(name, steps, warmup, B, W, dev, stream, graph=False, detail=True):
+    """Time one decode workload: K steps back to back between two events
+    (the value), each step alone (percentiles), each step after a cache flush
+    (workloads that fit the device cache), and a pass with every library
+    launch bracketed by events (kernel averages)."""
+    import torch
+    w = W.make_workload(name)
+    # Workloads whose per-step K/V fits the device cache twice over rotate over
+    # replicas, so that at least 4x the cache is touched between reuses.
+    replicas = 1
+    if w.kv_bytes_per_step() < 2 * MALL_BYTES:
+        replicas = min(16, max(2, math.ceil(4 * MALL_BYTES / w.kv_bytes_per_step())))
+    t0 = time.time()
+    xs = [Inputs(w, dev, B, stream) for _ in range(replicas)]
+    torch.cuda.synchronize()
+    print(f"[bench] {w.name}: pool {w.pool_bytes() / 1e9:.2f} GB x {replicas} replica(s), "
+          f"inputs made in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    with torch.cuda.stream(stream):
+        for i in range(max(warmup, replicas)):
+            run_step(w, xs[i % replicas], B, stream)
+    torch.cuda.synchronize()
+    if graph:
+        for x in xs:
+            capture_step(w, x, B, stream)
+        with torch.cuda.stream(stream):
+            for i in range(replicas):
+                run_step(w, xs[i % replicas], B, stream)
+        torch.cuda.synchronize()
+
+    # Timed region: K steps between two events on the launch stream.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        t_host0 = time.perf_counter()
+        for i in range(steps):
+            run_step(w, xs[i % replicas], B, stream)
+        t_host1 = time.perf_counter()
+        e1.record(stream)
+    e1.synchronize()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    kv_step = w.kv_bytes_per_step()
+    value = kv_step / (ms_step * 1e-3) / 1e9
+    res = {"workload": DECODE_NAMES[name], "w": w, "replicas": replicas, "ms_per_step": ms_step,
+           "value": value, "kv_bytes_per_step": kv_step,
+           "host_us_per_step": (t_host1 - t_host0) / steps * 1e6}
+    run_one = lambda i: run_step(w, xs[i % replicas], B, stream)
+    if detail:
+        res["pct"] = step_percentiles(run_one, steps, stream)
+    res["flushed"] = None
+    if replicas > 1:
+        fl = flushed_steps(run_one, steps, stream, dev)
+        res["flushed"] = {"us_per_step": fl, "GBps_at_p50": round(kv_step / (fl["p50"] * 1e-6) / 1e9, 1),
+                          "note": "each step timed alone after a 1 GiB write that evicts the device cache"}
+    # Kernel durations: the same K steps again with every kernel the library
+    # queues bracketed by HIP events on the launch stream (the brackets add
+    # small gaps between kernels, so the step time above is taken without
+    # them). This pass launches eagerly: graph replays bypass the brackets.
+    for x in xs:
+        x.graph = None
+    B.profile_start()
+    with torch.cuda.stream(stream):
+        for i in range(steps):
+            run_step(w, xs[i % replicas], B, stream)
+    torch.cuda.synchronize()
+    prof = B.profile_stop()
+    res["prof"] = prof
+    dec_ms, dec_n = prof["decode"]
+    res["decode_avg_ms"] = dec_ms / max(dec_n, 1)
+    mer_ms, mer_n = prof["merge"]
+    app_ms, app_n = prof["append"]
+    res["kernels_us_per_step"] = {"decode": round(dec_ms / steps * 1e3, 1), "merge": round(mer_ms / steps * 1e3, 1),
+                                  "append": round(app_ms / steps * 1e3, 1)}
+    print(f"[bench] {name}: step {ms_step * 1e3:.1f} us (host {res['host_us_per_step']:.1f} us); decode "
+          f"kernel avg {res['decode_avg_ms'] * 1e3:.1f} us x {dec_n}, merge "
+          f"{mer_ms / max(mer_n, 1) * 1e3:.1f} us x {mer_n}, append {app_ms / max(app_n, 1) * 1e3:.1f} us x "
+          f"{app_n}", file=sys.stderr, flush=True)
+    del xs
+    torch.cuda.empty_cache()
+    return res
+
+
+def config_summary(res):
+    w = res["w"]
+    dec_us = res["decode_avg_ms"] * 1e3
+    out = {
+        "workload": res["workload"],
+        "us_per_step": round(res["ms_per_step"] * 1e3, 2),
+        "kv_GBps": round(res["value"], 1),
+        "frac_of_hbm_peak": round(res["value"] / HBM_PEAK_GBPS, 4),
+        "decode_kernel_avg_us": round(dec_us, 2),
+        "decode_kernel_GBps": round(w.kv_bytes_per_layer() / (dec_us * 1e-6) / 1e9, 1),
+        "kernels_us_per_step": res["kernels_us_per_step"],
+        "host_us_per_step": round(res["host_us_per_step"], 1),
+        "kv_bytes_per_step": res["kv_bytes_per_step"],
+        "replicas": res["replicas"],
+    }
+    if res.get("flushed"):
+        out["cache_flushed_p50_us"] = res["flushed"]["us_per_step"]["p50"]
+        out["cache_flushed_GBps_at_p50"] = res["flushed"]["GBps_at_p50"]
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -504,75 +645,17 @@ def main():
         raise RuntimeError("bench.py needs a GPU")
     dev = torch.device("cuda:0")
     B.lib()
-    w = W.make_workload(args.workload)
     stream = torch.cuda.Stream(device=dev)     # default priority
 
-    # Workloads whose per-step K/V fits the device cache twice over rotate over
-    # replicas, so that at least 4x the cache is touched between reuses.
-    replicas = 1
-    if w.kv_bytes_per_step() < 2 * MALL_BYTES:
-        replicas = min(16, max(2, math.ceil(4 * MALL_BYTES / w.kv_bytes_per_step())))
-    t0 = time.time()
-    xs = [Inputs(w, dev, B) for _ in range(replicas)]
-    torch.cuda.synchronize()
-    gen_s = time.time() - t0
-    print(f"[bench] {w.name}: pool {w.pool_bytes() / 1e9:.2f} GB x {replicas} replica(s), "
-          f"inputs made in {gen_s:.1f} s", file=sys.stderr, flush=True)
-
-    with torch.cuda.stream(stream):
-        for i in range(max(args.warmup, replicas)):
-            run_step(w, xs[i % replicas], B, stream)
-    torch.cuda.synchronize()
-    if args.graph:
-        for x in xs:
-            capture_step(w, x, B, stream)
-        with torch.cuda.stream(stream):
-            for i in range(replicas):
-                run_step(w, xs[i % replicas], B, stream)
-        torch.cuda.synchronize()
-
-    # Timed region: K steps between two events on the launch stream.
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        for i in range(args.steps):
-            run_step(w, xs[i % replicas], B, stream)
-        e1.record(stream)
-    e1.synchronize()
-    torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    ms_step = ms_total / args.steps
-    kv_step = w.kv_bytes_per_step()
-    value = kv_step / (ms_step * 1e-3) / 1e9
-    pct = step_percentiles(lambda i: run_step(w, xs[i % replicas], B, stream), args.steps, stream)
-    flushed = None
-    if replicas > 1:
-        fl = flushed_steps(lambda i: run_step(w, xs[i % replicas], B, stream), args.steps, stream, dev)
-        flushed = {"us_per_step": fl, "GBps_at_p50": round(kv_step / (fl["p50"] * 1e-6) / 1e9, 1),
-                   "note": "each step timed alone after a 1 GiB write that evicts the device cache; "
-                           "the headline value rotates over replicas instead"}
-
-    # Kernel durations: the same K steps again with every kernel the library
-    # queues bracketed by HIP events on the launch stream (the brackets add
-    # small gaps between kernels, so the step time above is taken without them).
-    # This pass launches eagerly: graph replays bypass the library's brackets.
-    B.profile_start()
-    with torch.cuda.stream(stream):
-        for i in range(args.steps):
-            x = xs[i % replicas]
-            run_layers(w, x, B, stream, upload_plan(w, x, B, stream))
-    torch.cuda.synchronize()
-    prof = B.profile_stop()
-
-    dec_ms, dec_n = prof["decode"]
-    mer_ms, mer_n = prof["merge"]
-    app_ms, app_n = prof["append"]
-    dec_avg_ms = dec_ms / max(dec_n, 1)
-    achieved = w.kv_bytes_per_layer() / (dec_avg_ms * 1e-3) / 1e9
-    print(f"[bench] step {ms_step * 1e3:.1f} us; decode kernel avg {dec_avg_ms * 1e3:.1f} us x "
-          f"{dec_n}, merge {mer_ms / max(mer_n, 1) * 1e3:.1f} us x {mer_n}, append "
-          f"{app_ms / max(app_n, 1) * 1e3:.1f} us x {app_n}", file=sys.stderr, flush=True)
+    head = measure_decode(args.workload, args.steps, args.warmup, B, W, dev, stream, graph=args.graph)
+    w = head["w"]
+    configs = {}
+    if not args.no_configs:
+        for name in ("tiny", "c2", "c3", "c4", "c5"):
+            if name == args.workload:
+                continue
+            r = measure_decode(name, args.steps, args.warmup, B, W, dev, stream, detail=False)
+            configs[name] = config_summary(r)
 
     ceiling = ceiling_median = None
     if not args.no_ceiling:
@@ -582,7 +665,11 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
 
+    dec_avg_ms = head["decode_avg_ms"]
+    achieved = w.kv_bytes_per_layer() / (dec_avg_ms * 1e-3) / 1e9
     traffic = counted_traffic(w.name)
+    ms_step = head["ms_per_step"]
+    value = head["value"]
     result = {
         "metric": "paged decode attention: achieved KV-read GB/s (% of HBM peak) + us/step",
         "value": round(value, 1),
@@ -592,8 +679,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "us_per_step": round(ms_step * 1e3, 1),
-        "us_per_step_percentiles": pct,
-        "cache_flushed": flushed,
+        "us_per_step_percentiles": head.get("pct"),
+        "cache_flushed": head["flushed"],
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -601,12 +688,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": {"tiny": "tiny: 1 seq x ctx 128, 32q/8kv d64, 1 layer",
-                         "c2": "batch 8, ctx U[1,512], 32q/8kv d64, 1 layer",
-                         "c3": "batch 64, ctx U[256,2048], 32q/8kv d64, 1 layer",
-                         "c4": "full decode step: 16 layers x (append + decode), batch 256, "
-                               "ctx lognormal median 1024 clipped [16,8192], 32q/8kv d64",
-                         "c5": "batch 64, ctx U[4096,16384], 28q/4kv d128, 1 layer"}[w.name],
+            "workload": head["workload"],
             "global_batch": w.num_seqs,
             "layers": w.num_layers,
             "q_heads": w.num_q_heads,
@@ -614,15 +696,18 @@ def main():
             "head_dim": w.head_dim,
             "page_tokens": W.PAGE,
             "mean_ctx": round(float(w.ctx_lens.mean()), 1),
-            "kv_bytes_per_step": kv_step,
+            "kv_bytes_per_step": head["kv_bytes_per_step"],
             "pool_pages": w.num_pages,
-            "replicas": replicas,
-            "launch": "hip graph replay per step (plan copied before it)" if args.graph else "eager",
+            "replicas": head["replicas"],
+            "launch": ("hip graph replay per step (plan copied to the device before it)" if args.graph
+                       else "eager; plan made on the host each step, carried in the kernel arguments "
+                            "when it fits 1 KiB, else copied to the device once per step"),
+            "host_us_per_step": round(head["host_us_per_step"], 1),
             "parallelism": "single GPU",
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_split_kernel",
+            "kernel": "decode_kernel",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -630,16 +715,13 @@ def main():
             "traffic": traffic["traffic_bytes_per_launch"] if traffic else None,
             "traffic_detail": ({"fetch_bytes": traffic["fetch_bytes_per_launch"],
                                 "write_bytes": traffic["write_bytes_per_launch"],
-                                "source": "profiles/decode_split_kernel_c4.md"} if traffic else None),
+                                "source": "profiles/decode_kernel_c4.md"} if traffic else None),
             "avg_launch_us": round(dec_avg_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": w.kv_bytes_per_layer(),
         },
-        "kernels_us_per_step": {
-            "decode_split": round(dec_ms / args.steps * 1e3, 1),
-            "merge": round(mer_ms / args.steps * 1e3, 1),
-            "append": round(app_ms / args.steps * 1e3, 1),
-            "note": "separate profiled pass; each kernel bracketed by HIP events",
-        },
+        "kernels_us_per_step": dict(head["kernels_us_per_step"],
+                                    note="separate profiled pass; each kernel bracketed by HIP events"),
+        "configs": configs,
         "stream_read_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
         "stream_read_median_GBps": None if ceiling_median is None else round(ceiling_median, 1),
         "frac_of_stream_ceiling": None if ceiling is None else round(value / ceiling, 4),

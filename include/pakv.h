@@ -128,17 +128,20 @@ pa_status pa_kv_append(const pa_pool* pool, const void* k_new, const void* v_new
                        void* stream);
 
 /*
- * Bytes of workspace pa_decode needs for these sizes (0 when every possible
- * context fits one split). Long contexts are cut into splits of a fixed
- * number of tokens per head_dim (pa_split_tokens); each split's partial
- * softmax state is kept in the workspace and merged by log-sum-exp.
- * Returns 0 for a NULL pool or non-positive sizes.
+ * Bytes of workspace pa_decode needs for these sizes: 0 when no context can
+ * have more splits than one workgroup finishes itself (4 splits, or 2 when
+ * more than 8 query heads share a KV head). Contexts are cut into splits of
+ * a fixed number of tokens per head_dim (pa_split_tokens); the split
+ * partials of longer contexts are kept in the workspace and merged by
+ * log-sum-exp. Returns 0 for a NULL pool, non-positive sizes, or a query-head
+ * count that is not a multiple of the pool's KV heads.
  */
 size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs,
                                  int32_t num_q_heads, int32_t max_pages_per_seq);
 
-/* Tokens per split for a head_dim (64 or 128), 0 otherwise. Fixed per
- * head_dim, so a sequence's result never depends on the rest of the batch. */
+/* Tokens per split for a head_dim: 2048 at 64, 1024 at 128; 0 for others.
+ * Fixed per head_dim, so a sequence's result never depends on the rest of
+ * the batch. */
 int32_t pa_split_tokens(int32_t head_dim);
 
 /*
@@ -153,6 +156,16 @@ int32_t pa_split_tokens(int32_t head_dim);
  * pa_decode_workspace_bytes(...) bytes (may be NULL when that is 0); its
  * contents need no initialisation and are overwritten. Queued on `stream`.
  * num_seqs == 0 queues nothing.
+ *
+ * How the result is reduced (fixed per head_dim and group size, never by
+ * the batch): splits of pa_split_tokens tokens; inside a split, W logical
+ * waves (16 at head_dim 64, 8 at 128) each take every W-th pair of pages
+ * with their own online-softmax state, merged in logical-wave order; the
+ * splits of a sequence merged by log-sum-exp in split order. Without a plan
+ * one workgroup takes the splits of a sequence in groups of 4 (2 when more
+ * than 8 query heads share a KV head); a sequence with at most that many
+ * splits is finished inside its workgroup, a longer one by a second, merge
+ * kernel.
  */
 pa_status pa_decode(const pa_pool* pool, const void* q, int32_t num_seqs,
                     int32_t num_q_heads, const int32_t* block_tables,
@@ -161,14 +174,14 @@ pa_status pa_decode(const pa_pool* pool, const void* q, int32_t num_seqs,
                     size_t workspace_bytes, void* stream);
 
 /*
- * pa_kv_append followed by pa_decode, in one launch: decode adds the new
- * token to the cache and then attends over it (samir-vllm README review;
+ * pa_kv_append followed by pa_decode, in one call: decode adds the new token
+ * to the cache and then attends over it (samir-vllm README review;
  * news-factory.app course article, KV-cache section). Arguments are those of
- * the two calls; k_new / v_new / positions as in pa_kv_append. The pool after
- * the call and `out` are bit-identical to those of the two separate calls.
- * The workgroup whose split contains positions[b] writes the token before it
- * reads any page, so context_lens[b] may include the new token (the usual
- * case: positions[b] == context_lens[b] - 1).
+ * the two calls; k_new / v_new / positions as in pa_kv_append; every
+ * argument of both is checked before either is queued. Queues the append
+ * kernel, then the decode, so the pool after the call and `out` are
+ * bit-identical to those of the two separate calls, and context_lens[b] may
+ * include the new token (the usual case: positions[b] == context_lens[b] - 1).
  */
 pa_status pa_decode_append(const pa_pool* pool, const void* q, const void* k_new,
                            const void* v_new, const int32_t* positions, int32_t num_seqs,
@@ -178,49 +191,70 @@ pa_status pa_decode_append(const pa_pool* pool, const void* q, const void* k_new
                            size_t workspace_bytes, void* stream);
 
 /*
- * Launch plan (host side, optional). The workgroups of pa_decode cover every
- * (sequence, split) the batch could have, in split-major order; most of them
- * find their split empty when contexts are short next to max_pages_per_seq,
- * and the largest splits of the longest sequences start last. A plan lists
- * only the splits that exist, largest first (page count descending; ties in
- * sequence order, then split order; a sequence with an empty context keeps
- * one item, last, which writes its zero output). When the whole grid fits
- * the device at once (items x num_kv_heads <= 256 CUs x the decode
- * workgroups a CU holds: 4 at head_dim 64, 2 at 128), every other tier of 32
- * items (the CUs of one XCD) is reversed, so that each CU's items pair large
- * with small. Serving code knows its context lengths on the host, and one
- * plan serves every layer of a step.
+ * Launch plan (host side, optional). Without one, pa_decode runs one
+ * workgroup per sequence and group of splits, however uneven the contexts.
+ * A plan packs the batch's units (one split of one sequence each) into work
+ * items of up to 4 units (2 when more than 8 query heads share a KV head),
+ * one workgroup per item and KV head, so that the workgroups carry even
+ * work: a sequence with at most that many splits stays whole in one item
+ * (finished inside its workgroup, as without a plan); the splits of a longer
+ * one are placed one by one. Units go largest first to the item with the
+ * fewest page pairs that has room, over one round of the device (256 CUs,
+ * one decode workgroup each) times the rounds the unit count needs; items
+ * are listed by pairs, largest first. Each item also carries, per unit, the
+ * count of pairs before it (mod the waves per workgroup), so the
+ * workgroup's waves deal all of the item's pairs round-robin. Serving code
+ * knows its context lengths on the host, and one plan serves every layer of
+ * a step.
  *
- * pa_decode_plan_capacity: items a plan may need for these sizes
- * (num_seqs * splits per sequence), or -1 when the sizes are out of range
- * (num_seqs above 2^20, or more than 2^11 splits per sequence).
+ * pa_decode_plan_capacity: int32 words a plan may need for these sizes
+ * (8 per possible unit: num_seqs * splits per sequence * 8), or -1 when the
+ * sizes are out of range (num_seqs above 2^20, or more than 2^11 splits per
+ * sequence).
  * pa_decode_plan: writes the plan for the host array context_lens_host
  * [num_seqs] (values clamped into [0, max_pages_per_seq * 16], as the
- * kernel does) into plan[capacity] (host memory) and its length into
- * *num_items. Item encoding: b | (split << 20). Pure host code; queues
- * nothing.
+ * kernel does) and num_q_heads into plan[capacity] (host memory) and its
+ * length in int32 words into *num_ints. Item encoding, 8 words: units
+ * b | (split << 20), or -1 for none, in words 0..3; the units' rotations,
+ * 4 bits each, in word 4; words 5..7 zero. Pure host code; queues nothing.
  */
 int64_t pa_decode_plan_capacity(const pa_pool* pool, int32_t num_seqs,
                                 int32_t max_pages_per_seq);
 pa_status pa_decode_plan(const pa_pool* pool, const int32_t* context_lens_host,
-                         int32_t num_seqs, int32_t max_pages_per_seq, int32_t* plan,
-                         int64_t capacity, int32_t* num_items);
+                         int32_t num_seqs, int32_t num_q_heads, int32_t max_pages_per_seq,
+                         int32_t* plan, int64_t capacity, int32_t* num_ints);
 
 /*
  * pa_decode driven by a plan: the same arguments, plus plan (device memory,
- * int32 [num_items], a copy of what pa_decode_plan wrote) and num_items.
- * The output is bit-identical to pa_decode's when the plan was made from the
- * same context lengths (the splits, and the order in which they are merged,
- * do not change). A plan made from other lengths leaves the output of the
- * sequences it misses unwritten; items naming a sequence or split out of
- * range are skipped on the device.
+ * int32 [num_ints], a copy of what pa_decode_plan wrote for the same context
+ * lengths and num_q_heads) and num_ints (a multiple of 8). The output is
+ * bit-identical to pa_decode's: the splits, the logical waves and the merge
+ * order do not depend on which workgroup runs a unit. A plan made from other
+ * lengths leaves the output of the sequences it misses unwritten; units
+ * naming a sequence or split out of range are skipped on the device.
  */
 pa_status pa_decode_planned(const pa_pool* pool, const void* q, int32_t num_seqs,
                             int32_t num_q_heads, const int32_t* block_tables,
                             int32_t max_pages_per_seq, const int32_t* context_lens,
                             float scale, float* out, void* workspace,
                             size_t workspace_bytes, const int32_t* plan,
-                            int32_t num_items, void* stream);
+                            int32_t num_ints, void* stream);
+
+/*
+ * pa_decode_planned with the plan in host memory (plan_host: what
+ * pa_decode_plan wrote, num_ints <= 2048 words, i.e. at most 256 items). The
+ * plan travels by value in the decode kernel's arguments, which the HIP
+ * runtime copies when the launch is queued: nothing is copied to device
+ * memory beforehand, no device plan buffer is needed, and plan_host may be
+ * reused or freed as soon as the call returns. Larger plans give
+ * PA_ERR_INVALID (use pa_decode_planned). Same results, bit for bit.
+ */
+pa_status pa_decode_planned_host(const pa_pool* pool, const void* q, int32_t num_seqs,
+                                 int32_t num_q_heads, const int32_t* block_tables,
+                                 int32_t max_pages_per_seq, const int32_t* context_lens,
+                                 float scale, float* out, void* workspace,
+                                 size_t workspace_bytes, const int32_t* plan_host,
+                                 int32_t num_ints, void* stream);
 
 /*
  * Paged prefill. A chunk of new tokens per sequence: prefill fills a

@@ -30,7 +30,7 @@ EXPORTS = ["pa_pool_create", "pa_pool_destroy", "pa_kv_append", "pa_decode_works
            "pa_sched_submit_shared", "pa_sched_admit", "pa_sched_slot", "pa_sched_advance",
            "pa_sched_finish", "pa_sched_block_tables", "pa_sched_context_lens", "pa_sched_stats",
            "pa_kv_write", "pa_prefill", "pa_prefill_plan_capacity", "pa_prefill_plan",
-           "pa_prefill_planned"]
+           "pa_prefill_planned", "pa_decode_planned_host"]
 
 _lib = None
 
@@ -79,13 +79,15 @@ def lib() -> ctypes.CDLL:
     L.pa_stream_read.restype = c.c_int
     L.pa_decode_plan_capacity.argtypes = [c.c_void_p, c.c_int32, c.c_int32]
     L.pa_decode_plan_capacity.restype = c.c_int64
-    L.pa_decode_plan.argtypes = [c.c_void_p, c.c_void_p, c.c_int32, c.c_int32, c.c_void_p, c.c_int64,
-                                 c.POINTER(c.c_int32)]
+    L.pa_decode_plan.argtypes = [c.c_void_p, c.c_void_p, c.c_int32, c.c_int32, c.c_int32, c.c_void_p,
+                                 c.c_int64, c.POINTER(c.c_int32)]
     L.pa_decode_plan.restype = c.c_int
     L.pa_decode_planned.argtypes = [c.c_void_p, c.c_void_p, c.c_int32, c.c_int32, c.c_void_p, c.c_int32,
                                     c.c_void_p, c.c_float, c.c_void_p, c.c_void_p, c.c_size_t,
                                     c.c_void_p, c.c_int32, c.c_void_p]
     L.pa_decode_planned.restype = c.c_int
+    L.pa_decode_planned_host.argtypes = list(L.pa_decode_planned.argtypes)
+    L.pa_decode_planned_host.restype = c.c_int
     i32p, i64p = c.POINTER(c.c_int32), c.POINTER(c.c_int64)
     L.pa_sched_create.argtypes = [c.POINTER(c.c_void_p), c.c_int32, c.c_int32, c.c_int32, c.c_int32,
                                   c.c_int32]
@@ -288,16 +290,17 @@ def decode(pool: Pool, q, block_tables, context_lens, scale: float, out=None, wo
 
 
 def decode_plan_capacity(pool: Pool, num_seqs: int, max_pages_per_seq: int) -> int:
+    """int32 words a decode plan may need (pa_decode_plan_capacity)."""
     cap = int(lib().pa_decode_plan_capacity(pool.handle, int(num_seqs), int(max_pages_per_seq)))
     if cap < 0:
         raise PakvError(PA_ERR_INVALID, "pa_decode_plan_capacity")
     return cap
 
 
-def decode_plan_into(pool: Pool, context_lens_host, max_pages_per_seq: int, out) -> int:
+def decode_plan_into(pool: Pool, context_lens_host, num_q_heads: int, max_pages_per_seq: int, out) -> int:
     """Write the launch plan for these host context lengths into ``out`` (host
     int32 memory: a numpy array or a CPU torch tensor, e.g. pinned, of at least
-    decode_plan_capacity items); returns the number of items (pa_decode_plan)."""
+    decode_plan_capacity words); returns the number of words (pa_decode_plan)."""
     import numpy as np
     ctx = np.ascontiguousarray(np.asarray(context_lens_host, dtype=np.int32))
     if ctx.ndim != 1:
@@ -312,18 +315,19 @@ def decode_plan_into(pool: Pool, context_lens_host, max_pages_per_seq: int, out)
             raise ValueError("out must be a contiguous host int32 tensor")
         addr, size = out.data_ptr(), out.numel()
     n = ctypes.c_int32(0)
-    _check(lib().pa_decode_plan(pool.handle, ctx.ctypes.data, ctx.size, int(max_pages_per_seq),
-                                addr, size, ctypes.byref(n)), "pa_decode_plan")
+    _check(lib().pa_decode_plan(pool.handle, ctx.ctypes.data, ctx.size, int(num_q_heads),
+                                int(max_pages_per_seq), addr, size, ctypes.byref(n)), "pa_decode_plan")
     return n.value
 
 
-def decode_plan(pool: Pool, context_lens_host, max_pages_per_seq: int):
+def decode_plan(pool: Pool, context_lens_host, num_q_heads: int, max_pages_per_seq: int):
     """Host-side launch plan for these context lengths (pa_decode_plan): an int32
-    numpy array of items ``b | split << 20``, largest split first."""
+    numpy array of work items, 8 words each (units ``b | split << 20`` or -1,
+    then their rotations), the largest item first."""
     import numpy as np
     num_seqs = np.asarray(context_lens_host).size
     plan = np.zeros(max(decode_plan_capacity(pool, num_seqs, max_pages_per_seq), 1), dtype=np.int32)
-    n = decode_plan_into(pool, context_lens_host, max_pages_per_seq, plan)
+    n = decode_plan_into(pool, context_lens_host, num_q_heads, max_pages_per_seq, plan)
     return plan[:n].copy()
 
 
@@ -352,6 +356,170 @@ def decode_planned(pool: Pool, q, block_tables, context_lens, scale: float, plan
                                    ws_bytes, _ptr(plan), plan.numel(), _stream(stream)),
            "pa_decode_planned")
     return out
+
+
+def _host_plan_array(plan_host):
+    import numpy as np
+    if not isinstance(plan_host, np.ndarray) or plan_host.dtype != np.int32 or plan_host.ndim != 1 \
+            or not plan_host.flags.c_contiguous:
+        raise ValueError("plan_host must be a contiguous 1-D int32 numpy array")
+    return plan_host
+
+
+def decode_planned_host(pool: Pool, q, block_tables, context_lens, scale: float, plan_host, out=None,
+                        workspace=None, stream=None):
+    """pa_decode driven by a plan in host memory (pa_decode_planned_host):
+    ``plan_host`` is the int32 numpy array decode_plan returned (at most 2048
+    words); it travels in the kernel's arguments, so no device copy is made."""
+    import torch
+    _need(q, "q", _bf16_types(), 3)
+    _need(block_tables, "block_tables", (torch.int32,), 2)
+    _need(context_lens, "context_lens", (torch.int32,), 1)
+    plan_host = _host_plan_array(plan_host)
+    _check_decode_args(pool, q, block_tables, context_lens, out)
+    num_seqs, num_q_heads, d = q.shape
+    stride = block_tables.shape[1]
+    if out is None:
+        out = torch.empty((num_seqs, num_q_heads, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,), 3)
+    need = decode_workspace_bytes(pool, num_seqs, num_q_heads, stride)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode_planned_host(pool.handle, _ptr(q), num_seqs, num_q_heads, _ptr(block_tables),
+                                        stride, _ptr(context_lens), float(scale), _ptr(out), _ptr(workspace),
+                                        ws_bytes, plan_host.ctypes.data, plan_host.size, _stream(stream)),
+           "pa_decode_planned_host")
+    return out
+
+
+class HostPlan:
+    """A host buffer for the decode plans of one batch shape, remade by one C
+    call (pa_decode_plan) from the current contents of ``context_lens_host``
+    (a contiguous int32 numpy array the caller keeps updating). ``make()``
+    returns the plan's length in words; the words are in ``buf``."""
+
+    def __init__(self, pool: Pool, context_lens_host, num_q_heads: int, max_pages_per_seq: int):
+        import numpy as np
+        ctx = context_lens_host
+        if not isinstance(ctx, np.ndarray) or ctx.dtype != np.int32 or ctx.ndim != 1 or not ctx.flags.c_contiguous:
+            raise ValueError("context_lens_host must be a contiguous 1-D int32 numpy array")
+        self.ctx = ctx
+        self.cap = decode_plan_capacity(pool, ctx.size, max_pages_per_seq)
+        self.buf = np.zeros(max(self.cap, 1), dtype=np.int32)
+        self.words = 0
+        self._n = ctypes.c_int32(0)
+        self._call = (lib().pa_decode_plan, pool.handle, ctx.ctypes.data, ctx.size, int(num_q_heads),
+                      int(max_pages_per_seq), self.buf.ctypes.data, self.cap, ctypes.byref(self._n))
+        self._pool = pool   # keeps the descriptor alive
+
+    def make(self) -> int:
+        f, *args = self._call
+        _check(f(*args), "pa_decode_plan")
+        self.words = self._n.value
+        return self.words
+
+
+INLINE_PLAN_WORDS = 2048   # plans this small travel in the kernel's arguments (8 KiB)
+
+
+class DevicePlan:
+    """A HostPlan plus a device copy: ``upload(stream)`` remakes the plan on the
+    host, stages it in one of two pinned buffers and queues its copy to the
+    device buffer on ``stream`` (a staging buffer is reused only after the copy
+    that read it has run). For plans too large to travel in the kernel's
+    arguments; one upload serves every layer of a step."""
+
+    def __init__(self, pool: Pool, context_lens_host, num_q_heads: int, max_pages_per_seq: int, device):
+        import torch
+        self.host = HostPlan(pool, context_lens_host, num_q_heads, max_pages_per_seq)
+        self.ctx = self.host.ctx
+        cap = max(self.host.cap, 1)
+        self.pinned = [torch.empty(cap, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self.pinned_np = [t.numpy() for t in self.pinned]
+        self.done = [None, None]
+        self.dev = torch.empty(cap, dtype=torch.int32, device=device)
+        self.words = 0
+        self._k = 0
+
+    def upload(self, stream) -> int:
+        import torch
+        words = self.host.make()
+        k = self._k
+        self._k ^= 1
+        if self.done[k] is not None:
+            self.done[k].synchronize()
+        self.pinned_np[k][:words] = self.host.buf[:words]
+        with torch.cuda.stream(stream):
+            self.dev[:words].copy_(self.pinned[k][:words], non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record(stream)
+        self.done[k] = ev
+        self.words = words
+        return words
+
+
+class PreparedDecode:
+    """A planned decode launch with its arguments checked and marshalled once:
+    calling it queues the decode of this layer with the plan's current words,
+    pa_decode_planned_host for a HostPlan (the plan in the kernel's
+    arguments; at most 2048 words) or pa_decode_planned for a DevicePlan. The
+    tensors must stay alive and unchanged in shape (their contents may
+    change)."""
+
+    def __init__(self, pool: Pool, q, block_tables, context_lens, scale: float, plan, out,
+                 workspace=None, stream=None):
+        import torch
+        _need(q, "q", _bf16_types(), 3)
+        _need(block_tables, "block_tables", (torch.int32,), 2)
+        _need(context_lens, "context_lens", (torch.int32,), 1)
+        _need(out, "out", (torch.float32,), 3)
+        _check_decode_args(pool, q, block_tables, context_lens, out)
+        num_seqs, num_q_heads, _ = q.shape
+        if plan.ctx.size != num_seqs:
+            raise ValueError("the plan is for another batch size")
+        stride = block_tables.shape[1]
+        need = decode_workspace_bytes(pool, num_seqs, num_q_heads, stride)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        if ws_bytes < need:
+            raise ValueError(f"workspace of {ws_bytes} bytes, {need} needed")
+        self._keep = (pool, q, block_tables, context_lens, out, workspace, plan)
+        self._plan = plan
+        on_device = isinstance(plan, DevicePlan)
+        self._name = "pa_decode_planned" if on_device else "pa_decode_planned_host"
+        self._f = getattr(lib(), self._name)
+        self._args = (pool.handle, _ptr(q), num_seqs, num_q_heads, _ptr(block_tables), stride,
+                      _ptr(context_lens), float(scale), _ptr(out), _ptr(workspace), ws_bytes,
+                      _ptr(plan.dev) if on_device else plan.buf.ctypes.data)
+        self._stream = _stream(stream)
+
+    def __call__(self):
+        st = self._f(*self._args, self._plan.words, self._stream)
+        if st != PA_OK:
+            raise PakvError(st, self._name)
+
+
+class PreparedAppend:
+    """pa_kv_append with its arguments checked and marshalled once."""
+
+    def __init__(self, pool: Pool, k_new, v_new, block_tables, positions, stream=None):
+        import torch
+        _need(k_new, "k_new", _bf16_types(), 3)
+        _need(v_new, "v_new", _bf16_types(), 3)
+        _need(block_tables, "block_tables", (torch.int32,), 2)
+        _need(positions, "positions", (torch.int32,), 1)
+        num_seqs = block_tables.shape[0]
+        _check_new_rows(pool, num_seqs, k_new, v_new, positions)
+        _same_device(pool, block_tables)
+        self._keep = (pool, k_new, v_new, block_tables, positions)
+        self._f = lib().pa_kv_append
+        self._args = (pool.handle, _ptr(k_new), _ptr(v_new), num_seqs, _ptr(block_tables), block_tables.shape[1],
+                      _ptr(positions), _stream(stream))
+
+    def __call__(self):
+        st = self._f(*self._args)
+        if st != PA_OK:
+            raise PakvError(st, "pa_kv_append")
 
 
 def _chunk_common(q_or_k, query_start, block_tables, context_lens, max_chunk):

@@ -15,19 +15,10 @@
 #include "pakv_kernels.h"
 #include "pakv_prefill.h"
 
-// Split geometry per head_dim: pages per split and wavefronts per workgroup.
-// Fixed per head_dim so that a sequence's result does not depend on the batch.
-#ifndef PAKV_SPLIT_PAGES_D64
-#define PAKV_SPLIT_PAGES_D64 64
-#endif
-#ifndef PAKV_WAVES_D64
-#define PAKV_WAVES_D64 4
-#endif
-#ifndef PAKV_SPLIT_PAGES_D128
-#define PAKV_SPLIT_PAGES_D128 64
-#endif
-#ifndef PAKV_WAVES_D128
-#define PAKV_WAVES_D128 4
+// Rounds of work items (one decode workgroup per CU) the launch plan aims
+// for when it packs units into items: more rounds, smaller items.
+#ifndef PAKV_PLAN_ROUNDS
+#define PAKV_PLAN_ROUNDS 1
 #endif
 
 struct pa_pool {
@@ -56,7 +47,10 @@ bool scale_ok(float scale) { return std::isfinite(scale) && std::isfinite(scale_
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-int split_pages(int d) { return d == 64 ? PAKV_SPLIT_PAGES_D64 : PAKV_SPLIT_PAGES_D128; }
+int split_pages(int d) {
+  return d == 64 ? pakv::DecodeGeom<64>::SPLIT_PAGES : pakv::DecodeGeom<128>::SPLIT_PAGES;
+}
+int decode_waves(int d) { return d == 64 ? pakv::DecodeGeom<64>::W : pakv::DecodeGeom<128>::W; }
 
 // prefill workgroups (4 waves) one CU holds at once
 int prefill_wgs_per_cu(int d) {
@@ -64,9 +58,7 @@ int prefill_wgs_per_cu(int d) {
 }
 
 // decode workgroups one CU holds at once (waves per SIMD x 4 SIMDs / waves per workgroup)
-int decode_wgs_per_cu(int d) {
-  return pakv::occupancy(d) * 4 / (d == 64 ? PAKV_WAVES_D64 : PAKV_WAVES_D128);
-}
+int decode_wgs_per_cu(int d) { return std::max(1, pakv::occupancy(d) * 4 / decode_waves(d)); }
 
 int64_t splits_for(int d, int32_t max_pages_per_seq) {
   const int64_t sp = split_pages(d);
@@ -75,11 +67,12 @@ int64_t splits_for(int d, int32_t max_pages_per_seq) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace: partial accumulators [B][Hq][S][D] then (m, l) pairs [B][Hq][S][2].
-void workspace_parts(int d, int32_t num_seqs, int32_t num_q_heads, int32_t max_pages_per_seq,
+// Workspace: partial accumulators [B][Hq][S][D] then (m, l) pairs [B][Hq][S][2],
+// needed only when a sequence can have more splits than a work item holds.
+void workspace_parts(int d, int32_t num_seqs, int32_t num_q_heads, int group, int32_t max_pages_per_seq,
                      size_t* acc_bytes, size_t* total) {
   const int64_t s = splits_for(d, max_pages_per_seq);
-  if (s <= 1) {
+  if (s <= pakv::units_cap(group)) {
     *acc_bytes = 0;
     *total = 0;
     return;
@@ -137,35 +130,56 @@ struct LaunchTimer {
   }
 };
 
-template <int D, int W, int SP>
-pa_status launch_decode(const pakv::DecodeArgs& args, int64_t units, hipStream_t stream) {
+template <int D, int NW>
+pa_status launch_decode_with(const pakv::DecodeArgs& args, const pakv::InlinePlan<NW>& ip, int64_t items,
+                             hipStream_t stream) {
   (void)hipGetLastError();
-  const int64_t blocks = static_cast<int64_t>(args.num_kv_heads) * units;
-  if (blocks == 0) return PA_OK;
-  if (blocks > INT_MAX) return PA_ERR_INVALID;
-  const size_t lds = (2 * W * 16 + static_cast<size_t>(W) * args.group * (D + 4)) * sizeof(float);
+  if (items == 0) return PA_OK;
+  if (items > INT_MAX) return PA_ERR_INVALID;
   {
     LaunchTimer t(0, stream);
-    if (args.k_new)
-      hipLaunchKernelGGL((pakv::decode_split_kernel<D, W, SP, true>), dim3(static_cast<unsigned>(blocks)),
-                         dim3(64 * W), lds, stream, args);
-    else
-      hipLaunchKernelGGL((pakv::decode_split_kernel<D, W, SP, false>), dim3(static_cast<unsigned>(blocks)),
-                         dim3(64 * W), lds, stream, args);
+    // x: KV head, (y, z): work item (y below 65536)
+    const unsigned gy = static_cast<unsigned>(std::min<int64_t>(items, 65535));
+    const unsigned gz = static_cast<unsigned>((items + 65534) / 65535);
+    pakv::DecodeArgs a = args;
+    a.num_items = static_cast<int32_t>(items);
+    hipLaunchKernelGGL((pakv::decode_kernel<D, NW>), dim3(static_cast<unsigned>(args.num_kv_heads), gy, gz),
+                       dim3(64 * pakv::DecodeGeom<D>::W), 0, stream, a, ip);
   }
   if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
-  if (args.s_max > 1) {
-    const int64_t items = static_cast<int64_t>(args.num_seqs) * args.num_q_heads;
-    const int64_t mblocks = (items + 3) / 4;
+  if (args.s_max > args.ucap) {
+    const int64_t heads = static_cast<int64_t>(args.num_seqs) * args.num_q_heads;
+    const int64_t mblocks = (heads + 3) / 4;
     if (mblocks > INT_MAX) return PA_ERR_INVALID;
     {
       LaunchTimer t(1, stream);
       hipLaunchKernelGGL((pakv::merge_splits_kernel<D>), dim3(static_cast<unsigned>(mblocks)), dim3(256),
-                         0, stream, args, SP * pakv::kPage);
+                         0, stream, args);
     }
     if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
   }
   return PA_OK;
+}
+
+// plan_host: a host plan of plan_ints words to carry in the launch's
+// arguments (NULL: the device plan in args, or none)
+template <int D>
+pa_status launch_decode(const pakv::DecodeArgs& args, const int32_t* plan_host, int32_t plan_ints, int64_t items,
+                        hipStream_t stream) {
+  if (plan_host && plan_ints <= pakv::kInlineSmall) {
+    pakv::InlinePlan<pakv::kInlineSmall> ip;
+    std::copy(plan_host, plan_host + plan_ints, ip.w);
+    std::fill(ip.w + plan_ints, ip.w + pakv::kInlineSmall, 0);
+    return launch_decode_with<D>(args, ip, items, stream);
+  }
+  if (plan_host) {
+    pakv::InlinePlan<pakv::kInlineLarge> ip;
+    std::copy(plan_host, plan_host + plan_ints, ip.w);
+    std::fill(ip.w + plan_ints, ip.w + pakv::kInlineLarge, 0);
+    return launch_decode_with<D>(args, ip, items, stream);
+  }
+  pakv::InlinePlan<pakv::kItemInts> none{};
+  return launch_decode_with<D>(args, none, items, stream);
 }
 
 }  // namespace
@@ -217,8 +231,10 @@ int32_t pa_split_tokens(int32_t head_dim) {
 size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                  int32_t max_pages_per_seq) {
   if (!pool || num_seqs <= 0 || num_q_heads <= 0 || max_pages_per_seq <= 0) return 0;
+  if (num_q_heads % pool->num_kv_heads != 0) return 0;
   size_t acc = 0, total = 0;
-  workspace_parts(pool->head_dim, num_seqs, num_q_heads, max_pages_per_seq, &acc, &total);
+  workspace_parts(pool->head_dim, num_seqs, num_q_heads, num_q_heads / pool->num_kv_heads, max_pages_per_seq,
+                  &acc, &total);
   return total;
 }
 
@@ -257,13 +273,11 @@ pa_status pa_kv_append(const pa_pool* pool, const void* k_new, const void* v_new
   return PA_OK;
 }
 
-static pa_status decode_impl(const pa_pool* pool, const void* q, bool fused, const void* k_new,
-                             const void* v_new,
-                             const int32_t* positions, int32_t num_seqs, int32_t num_q_heads,
+static pa_status decode_impl(const pa_pool* pool, const void* q, int32_t num_seqs, int32_t num_q_heads,
                              const int32_t* block_tables, int32_t max_pages_per_seq,
                              const int32_t* context_lens, float scale, float* out, void* workspace,
-                             size_t workspace_bytes, const int32_t* plan, int32_t plan_items,
-                             void* stream) {
+                             size_t workspace_bytes, const int32_t* plan, const int32_t* plan_host,
+                             int32_t plan_ints, void* stream) {
   if (!pool) return PA_ERR_NULL;
   if (num_seqs < 0 || num_q_heads < 1 || max_pages_per_seq < 1) return PA_ERR_INVALID;
   if (static_cast<int64_t>(max_pages_per_seq) * pakv::kPage > INT_MAX) return PA_ERR_INVALID;
@@ -275,20 +289,18 @@ static pa_status decode_impl(const pa_pool* pool, const void* q, bool fused, con
   if (!q || !block_tables || !context_lens || !out) return PA_ERR_NULL;
   if (!aligned16(q) || !aligned4(block_tables) || !aligned4(context_lens) || !aligned16(out))
     return PA_ERR_ALIGN;
-  if (fused) {
-    if (!k_new || !v_new || !positions) return PA_ERR_NULL;
-    if (!aligned16(k_new) || !aligned16(v_new) || !aligned4(positions)) return PA_ERR_ALIGN;
-  }
   const int d = pool->head_dim;
   const int64_t s_max = splits_for(d, max_pages_per_seq);
   if (num_seqs > kPlanMaxSeqs || s_max > kPlanMaxSplits) {
-    if (plan) return PA_ERR_INVALID;
+    if (plan || plan_host) return PA_ERR_INVALID;
   }
-  if (plan_items < 0 || plan_items > static_cast<int64_t>(num_seqs) * s_max) return PA_ERR_INVALID;
-  if (plan_items > 0 && !plan) return PA_ERR_NULL;
+  if (plan_ints < 0 || plan_ints % pakv::kItemInts != 0) return PA_ERR_INVALID;
+  if (plan_ints > static_cast<int64_t>(num_seqs) * s_max * pakv::kItemInts) return PA_ERR_INVALID;
+  if (plan_host && plan_ints > pakv::kInlineLarge) return PA_ERR_INVALID;
+  if (plan_ints > 0 && !plan && !plan_host) return PA_ERR_NULL;
   if (plan && !aligned4(plan)) return PA_ERR_ALIGN;
   size_t acc_bytes = 0, need = 0;
-  workspace_parts(d, num_seqs, num_q_heads, max_pages_per_seq, &acc_bytes, &need);
+  workspace_parts(d, num_seqs, num_q_heads, group, max_pages_per_seq, &acc_bytes, &need);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return PA_ERR_ALIGN;
@@ -308,106 +320,176 @@ static pa_status decode_impl(const pa_pool* pool, const void* q, bool fused, con
   a.num_kv_heads = pool->num_kv_heads;
   a.group = group;
   a.stride = max_pages_per_seq;
-  a.s_max = static_cast<int32_t>(splits_for(d, max_pages_per_seq));
+  a.s_max = static_cast<int32_t>(s_max);
+  a.ucap = pakv::units_cap(group);
   a.scale_log2 = scale_log2_of(scale);
-  a.k_new = fused ? static_cast<const uint16_t*>(k_new) : nullptr;
-  a.v_new = fused ? static_cast<const uint16_t*>(v_new) : nullptr;
-  a.positions = fused ? positions : nullptr;
-  a.plan = plan;
-  const int64_t units = plan ? plan_items : static_cast<int64_t>(num_seqs) * s_max;
+  a.plan = plan_host ? nullptr : plan;
+  // work items: the plan's, or per sequence its splits in groups of ucap
+  const int64_t items = (plan || plan_host) ? plan_ints / pakv::kItemInts
+                                            : static_cast<int64_t>(num_seqs) * ((s_max + a.ucap - 1) / a.ucap);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (d == 64) return launch_decode<64, PAKV_WAVES_D64, PAKV_SPLIT_PAGES_D64>(a, units, s);
-  return launch_decode<128, PAKV_WAVES_D128, PAKV_SPLIT_PAGES_D128>(a, units, s);
+  if (d == 64) return launch_decode<64>(a, plan_host, plan_ints, items, s);
+  return launch_decode<128>(a, plan_host, plan_ints, items, s);
 }
 
 pa_status pa_decode(const pa_pool* pool, const void* q, int32_t num_seqs, int32_t num_q_heads,
                     const int32_t* block_tables, int32_t max_pages_per_seq,
                     const int32_t* context_lens, float scale, float* out, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  return decode_impl(pool, q, false, nullptr, nullptr, nullptr, num_seqs, num_q_heads, block_tables,
-                     max_pages_per_seq, context_lens, scale, out, workspace, workspace_bytes, nullptr,
-                     0, stream);
+  return decode_impl(pool, q, num_seqs, num_q_heads, block_tables, max_pages_per_seq, context_lens, scale, out,
+                     workspace, workspace_bytes, nullptr, nullptr, 0, stream);
 }
 
 int64_t pa_decode_plan_capacity(const pa_pool* pool, int32_t num_seqs, int32_t max_pages_per_seq) {
   if (!pool || num_seqs < 0 || max_pages_per_seq < 1) return -1;
   const int64_t s_max = splits_for(pool->head_dim, max_pages_per_seq);
   if (num_seqs > kPlanMaxSeqs || s_max > kPlanMaxSplits) return -1;
-  return static_cast<int64_t>(num_seqs) * s_max;
+  return static_cast<int64_t>(num_seqs) * s_max * pakv::kItemInts;
 }
 
 static pa_status decode_plan_impl(const pa_pool* pool, const int32_t* context_lens_host, int32_t num_seqs,
-                                  int32_t max_pages_per_seq, int32_t* plan, int64_t capacity,
-                                  int32_t* num_items);
+                                  int group, int32_t max_pages_per_seq, int32_t* plan, int64_t capacity,
+                                  int32_t* num_ints);
 
 pa_status pa_decode_plan(const pa_pool* pool, const int32_t* context_lens_host, int32_t num_seqs,
-                         int32_t max_pages_per_seq, int32_t* plan, int64_t capacity,
-                         int32_t* num_items) {
-  if (!pool || !num_items) return PA_ERR_NULL;
-  *num_items = 0;
+                         int32_t num_q_heads, int32_t max_pages_per_seq, int32_t* plan, int64_t capacity,
+                         int32_t* num_ints) {
+  if (!pool || !num_ints) return PA_ERR_NULL;
+  *num_ints = 0;
   const int64_t cap_needed = pa_decode_plan_capacity(pool, num_seqs, max_pages_per_seq);
   if (cap_needed < 0) return PA_ERR_INVALID;
+  if (num_q_heads < 1 || num_q_heads % pool->num_kv_heads != 0) return PA_ERR_INVALID;
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (group > kMaxGroup) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (!context_lens_host || !plan) return PA_ERR_NULL;
   try {
-    return decode_plan_impl(pool, context_lens_host, num_seqs, max_pages_per_seq, plan, capacity,
-                            num_items);
+    return decode_plan_impl(pool, context_lens_host, num_seqs, group, max_pages_per_seq, plan, capacity,
+                            num_ints);
   } catch (...) {   // out of host memory; nothing escapes the C ABI
-    *num_items = 0;
+    *num_ints = 0;
     return PA_ERR_INVALID;
   }
 }
 
+// The plan packs units (splits of one sequence) into work items of at most
+// ucap units, one workgroup per item and KV head:
+//  - a sequence of at most ucap splits is one indivisible group (its splits
+//    are merged inside the workgroup); a longer one gives one group per
+//    split (merged by the merge kernel);
+//  - groups go, largest first, to the item with the fewest pairs that has
+//    room for them, over as many items as one round of the device holds
+//    (256 CUs, one workgroup each, Hkv workgroups per item) times the rounds
+//    the unit count needs; an item runs out of room only by its unit count;
+//  - items are listed by pairs, largest first, so that a grid of several
+//    rounds ends on its smallest items.
+// A unit's rotation is the number of pairs before it in its item, mod W:
+// the workgroup's waves then deal all of the item's pairs round-robin.
 static pa_status decode_plan_impl(const pa_pool* pool, const int32_t* context_lens_host, int32_t num_seqs,
-                                  int32_t max_pages_per_seq, int32_t* plan, int64_t capacity,
-                                  int32_t* num_items) {
-  const int sp = split_pages(pool->head_dim);
+                                  int group, int32_t max_pages_per_seq, int32_t* plan, int64_t capacity,
+                                  int32_t* num_ints) {
+  const int d = pool->head_dim;
+  const int sp = split_pages(d);
+  const int W = decode_waves(d);
+  const int ucap = pakv::units_cap(group);
   const int64_t max_tok = static_cast<int64_t>(max_pages_per_seq) * pakv::kPage;
-  // pages of every split, then a counting sort by page count, largest first
-  // (ties in sequence order, then split order); an empty context keeps one
-  // unit (it writes the zero output) and goes last
-  std::vector<int64_t> count(sp + 2, 0);
-  int64_t total = 0;
+  struct Group {
+    int64_t pairs;
+    int32_t b, s0, units;
+  };
+  auto split_pairs = [&](int64_t pages, int64_t s) {
+    return (std::min<int64_t>(pages - s * sp, sp) + 1) / 2;
+  };
+  std::vector<Group> groups;
+  groups.reserve(static_cast<size_t>(num_seqs));
+  int64_t total_units = 0;
   for (int32_t b = 0; b < num_seqs; ++b) {
     const int64_t n = std::min<int64_t>(std::max(context_lens_host[b], 0), max_tok);
     const int64_t pages = (n + pakv::kPage - 1) / pakv::kPage;
-    if (pages == 0) {
-      ++count[0];
-      ++total;
-      continue;
-    }
     const int64_t ns = (pages + sp - 1) / sp;
-    count[sp] += ns - 1;
-    ++count[pages - (ns - 1) * sp];
-    total += ns;
-  }
-  if (total > capacity) return PA_ERR_INVALID;
-  std::vector<int64_t> start(sp + 2, 0);
-  int64_t acc = 0;
-  for (int pg = sp; pg >= 0; --pg) {
-    start[pg] = acc;
-    acc += count[pg];
-  }
-  for (int32_t b = 0; b < num_seqs; ++b) {
-    const int64_t n = std::min<int64_t>(std::max(context_lens_host[b], 0), max_tok);
-    const int64_t pages = (n + pakv::kPage - 1) / pakv::kPage;
-    const int64_t ns = pages == 0 ? 1 : (pages + sp - 1) / sp;
-    for (int64_t s = 0; s < ns; ++s) {
-      const int64_t pg = std::min<int64_t>(pages - s * sp, sp);
-      plan[start[pg]++] = static_cast<int32_t>(static_cast<uint32_t>(b) | (static_cast<uint32_t>(s) << 20));
+    if (ns <= 1) {   // an empty context keeps one unit: it writes the zero output
+      groups.push_back({ns ? split_pairs(pages, 0) : 0, b, 0, 1});
+      total_units += 1;
+    } else if (ns <= ucap) {
+      int64_t p = 0;
+      for (int64_t s = 0; s < ns; ++s) p += split_pairs(pages, s);
+      groups.push_back({p, b, 0, static_cast<int32_t>(ns)});
+      total_units += ns;
+    } else {
+      for (int64_t s = 0; s < ns; ++s) groups.push_back({split_pairs(pages, s), b, static_cast<int32_t>(s), 1});
+      total_units += ns;
     }
   }
-  // A grid the device holds all at once starts every workgroup together, and
-  // the workgroups reach the 8 XCDs round-robin, then a CU of their XCD in
-  // order: each CU gets items t, t + 32, t + 64, ... of its XCD's sequence.
-  // Reversing every other tier of 32 items pairs the large ones with small
-  // ones on each CU instead of stacking the large ones.
-  const int64_t resident = static_cast<int64_t>(kDeviceCUs) * decode_wgs_per_cu(pool->head_dim);
-  if (total * pool->num_kv_heads <= resident) {
-    for (int64_t t0 = kCUsPerXCD; t0 < total; t0 += 2 * kCUsPerXCD)
-      std::reverse(plan + t0, plan + std::min<int64_t>(t0 + kCUsPerXCD, total));
+  std::stable_sort(groups.begin(), groups.end(), [](const Group& x, const Group& y) { return x.pairs > y.pairs; });
+  const int64_t slots = std::max<int64_t>(1, kDeviceCUs * decode_wgs_per_cu(d) / pool->num_kv_heads);
+  const int64_t rounds = std::max<int64_t>(PAKV_PLAN_ROUNDS, (total_units + ucap * slots - 1) / (ucap * slots));
+  const int64_t nbins = std::min<int64_t>(static_cast<int64_t>(groups.size()), rounds * slots);
+  struct Bin {
+    int64_t pairs = 0;
+    int units = 0;
+    std::vector<int32_t> members;   // group indices, in the order placed
+  };
+  std::vector<Bin> bins(static_cast<size_t>(nbins));
+  // bins by free unit count, each a min-heap on (pairs, index)
+  typedef std::pair<int64_t, int64_t> Key;
+  std::vector<std::vector<Key>> heaps(static_cast<size_t>(ucap) + 1);
+  auto greater = [](const Key& x, const Key& y) { return x > y; };
+  for (int64_t i = 0; i < nbins; ++i) heaps[ucap].push_back({0, i});
+  for (size_t gi = 0; gi < groups.size(); ++gi) {
+    const Group& g = groups[gi];
+    int best_f = -1;
+    for (int f = g.units; f <= ucap; ++f)
+      if (!heaps[f].empty() && (best_f < 0 || heaps[f].front() < heaps[best_f].front())) best_f = f;
+    int64_t bi;
+    if (best_f < 0) {
+      bi = static_cast<int64_t>(bins.size());
+      bins.emplace_back();
+    } else {
+      std::pop_heap(heaps[best_f].begin(), heaps[best_f].end(), greater);
+      bi = heaps[best_f].back().second;
+      heaps[best_f].pop_back();
+    }
+    Bin& bin = bins[static_cast<size_t>(bi)];
+    bin.pairs += g.pairs;
+    bin.units += g.units;
+    bin.members.push_back(static_cast<int32_t>(gi));
+    const int f = ucap - bin.units;
+    if (f > 0) {
+      heaps[f].push_back({bin.pairs, bi});
+      std::push_heap(heaps[f].begin(), heaps[f].end(), greater);
+    }
   }
-  *num_items = static_cast<int32_t>(total);
+  std::vector<int64_t> order;
+  order.reserve(bins.size());
+  for (size_t i = 0; i < bins.size(); ++i)
+    if (!bins[i].members.empty()) order.push_back(static_cast<int64_t>(i));
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int64_t x, int64_t y) { return bins[static_cast<size_t>(x)].pairs > bins[static_cast<size_t>(y)].pairs; });
+  const int64_t ints = static_cast<int64_t>(order.size()) * pakv::kItemInts;
+  if (ints > capacity) return PA_ERR_INVALID;
+  int64_t w = 0;
+  for (int64_t bi : order) {
+    const Bin& bin = bins[static_cast<size_t>(bi)];
+    int32_t* it = plan + w;
+    for (int k = 0; k < pakv::kItemInts; ++k) it[k] = k < pakv::kItemUnits ? -1 : 0;
+    int u = 0;
+    int64_t before = 0;
+    uint32_t rot = 0;
+    for (int32_t gi : bin.members) {
+      const Group& g = groups[static_cast<size_t>(gi)];
+      const int64_t n = std::min<int64_t>(std::max(context_lens_host[g.b], 0), max_tok);
+      const int64_t pages = (n + pakv::kPage - 1) / pakv::kPage;
+      for (int32_t k = 0; k < g.units; ++k, ++u) {
+        const int64_t s = g.s0 + k;
+        it[u] = static_cast<int32_t>(static_cast<uint32_t>(g.b) | (static_cast<uint32_t>(s) << 20));
+        rot |= static_cast<uint32_t>(before % W) << (4 * u);
+        before += pages > 0 ? split_pairs(pages, s) : 0;
+      }
+    }
+    it[pakv::kItemUnits] = static_cast<int32_t>(rot);
+    w += pakv::kItemInts;
+  }
+  *num_ints = static_cast<int32_t>(ints);
   return PA_OK;
 }
 
@@ -415,12 +497,22 @@ pa_status pa_decode_planned(const pa_pool* pool, const void* q, int32_t num_seqs
                             int32_t num_q_heads, const int32_t* block_tables,
                             int32_t max_pages_per_seq, const int32_t* context_lens, float scale,
                             float* out, void* workspace, size_t workspace_bytes,
-                            const int32_t* plan, int32_t num_items, void* stream) {
+                            const int32_t* plan, int32_t num_ints, void* stream) {
   if (!pool) return PA_ERR_NULL;
   if (!plan && num_seqs > 0) return PA_ERR_NULL;
-  return decode_impl(pool, q, false, nullptr, nullptr, nullptr, num_seqs, num_q_heads, block_tables,
-                     max_pages_per_seq, context_lens, scale, out, workspace, workspace_bytes, plan,
-                     num_items, stream);
+  return decode_impl(pool, q, num_seqs, num_q_heads, block_tables, max_pages_per_seq, context_lens, scale, out,
+                     workspace, workspace_bytes, plan, nullptr, num_ints, stream);
+}
+
+pa_status pa_decode_planned_host(const pa_pool* pool, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                                 const int32_t* block_tables, int32_t max_pages_per_seq,
+                                 const int32_t* context_lens, float scale, float* out, void* workspace,
+                                 size_t workspace_bytes, const int32_t* plan_host, int32_t num_ints,
+                                 void* stream) {
+  if (!pool) return PA_ERR_NULL;
+  if (!plan_host && num_seqs > 0) return PA_ERR_NULL;
+  return decode_impl(pool, q, num_seqs, num_q_heads, block_tables, max_pages_per_seq, context_lens, scale, out,
+                     workspace, workspace_bytes, nullptr, plan_host, num_ints, stream);
 }
 
 pa_status pa_decode_append(const pa_pool* pool, const void* q, const void* k_new, const void* v_new,
@@ -428,9 +520,29 @@ pa_status pa_decode_append(const pa_pool* pool, const void* q, const void* k_new
                            const int32_t* block_tables, int32_t max_pages_per_seq,
                            const int32_t* context_lens, float scale, float* out, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  return decode_impl(pool, q, true, k_new, v_new, positions, num_seqs, num_q_heads, block_tables,
-                     max_pages_per_seq, context_lens, scale, out, workspace, workspace_bytes, nullptr,
-                     0, stream);
+  // every argument of both halves is checked before either is queued
+  if (!pool) return PA_ERR_NULL;
+  if (num_seqs < 0 || num_q_heads < 1 || max_pages_per_seq < 1) return PA_ERR_INVALID;
+  if (static_cast<int64_t>(max_pages_per_seq) * pakv::kPage > INT_MAX) return PA_ERR_INVALID;
+  if (!scale_ok(scale)) return PA_ERR_INVALID;
+  if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_INVALID;
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (group > kMaxGroup) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !block_tables || !context_lens || !out || !k_new || !v_new || !positions) return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned4(block_tables) || !aligned4(context_lens) || !aligned16(out) ||
+      !aligned16(k_new) || !aligned16(v_new) || !aligned4(positions))
+    return PA_ERR_ALIGN;
+  size_t acc_bytes = 0, need = 0;
+  workspace_parts(pool->head_dim, num_seqs, num_q_heads, group, max_pages_per_seq, &acc_bytes, &need);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PA_ERR_ALIGN;
+  }
+  pa_status st = pa_kv_append(pool, k_new, v_new, num_seqs, block_tables, max_pages_per_seq, positions, stream);
+  if (st != PA_OK) return st;
+  return decode_impl(pool, q, num_seqs, num_q_heads, block_tables, max_pages_per_seq, context_lens, scale, out,
+                     workspace, workspace_bytes, nullptr, nullptr, 0, stream);
 }
 
 // Shared validation of a chunked (prefill / chunk write) call.

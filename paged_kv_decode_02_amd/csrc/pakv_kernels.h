@@ -7,11 +7,28 @@
 // contiguous grouped-query heads ("Construye tu propio motor de inferencia LLM
 // ..." (aibit.im), section "Atención de Consulta Agrupada (GQA)").
 //
-// Work decomposition. A context is cut into splits of SPLIT_PAGES pages (a
-// fixed count per head_dim). One workgroup of W wavefronts handles one
-// (split, sequence, KV head); wave w takes page pairs w, w + W, ... of the
-// split. Per page pair (32 tokens) a wave does:
+// Reduction structure (fixed per head_dim, so a sequence's result never
+// depends on the rest of the batch). A context is cut into splits of
+// SPLIT_PAGES pages. Inside a split, logical wave lw (0 <= lw < W) streams
+// page pairs lw, lw + W, lw + 2 W, ... with its own online-softmax state; the
+// W partial states of a split are merged in logical-wave order, and the
+// splits of a sequence by log-sum-exp in split order.
 //
+// Work decomposition. One workgroup of W wavefronts takes one work item: up
+// to four units of one KV head, a unit being one split of one sequence.
+// Physical wave p runs logical wave (p - rot_u) mod W of every unit u in
+// turn, so that the pairs of all the item's units are dealt round-robin over
+// the W waves (rot_u, from the launch plan, is the running count of pairs
+// before unit u, mod W) and every wave gets the same count to within one.
+// A wave's pairs form one stream: the next pair is always in flight while
+// the current one is computed, across unit boundaries too. At a unit's end
+// the wave parks its partial state in LDS. When every wave is done, the
+// workgroup merges each unit's W partials; a sequence whose splits all lie
+// in the item (at most four; two when G > 8) is finished in LDS, by the
+// same log-sum-exp code the merge kernel runs for longer sequences, whose
+// split partials go to the workspace.
+//
+// Per page pair (32 tokens), per wave:
 //   QK^T on the matrix cores, v_mfma_f32_16x16x32_bf16 with
 //     A = 16 key rows (tokens) x 32 head dims, B = 32 head dims x 16 columns
 //     (the G query heads of the group, zero-padded to 16), so
@@ -25,10 +42,7 @@
 //
 // Every K/V byte is loaded once, 16 bytes per lane per load, straight into the
 // registers of its MFMA operand, with the nontemporal (streaming) hint where
-// it measured faster; the next pair's loads are issued before the current
-// pair is computed. Waves merge (m, l, acc) through LDS; a split that
-// is not alone writes its partial to the workspace and merge_splits combines
-// the splits of a sequence by log-sum-exp in split order.
+// it measured faster.
 //
 // Lane roles (lane = 0..63, r = lane % 16, grp = lane / 16):
 //   QK A operand   row r = token: page (r / 8) of the pair,
@@ -60,6 +74,26 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Decode geometry per head_dim: pages per split and waves per workgroup
+// (= logical waves per split). Both give at most 4 page pairs per logical
+// wave of a full split.
+template <int D> struct DecodeGeom;
+template <> struct DecodeGeom<64> {
+  static constexpr int W = 16;
+  static constexpr int SPLIT_PAGES = 128;
+};
+template <> struct DecodeGeom<128> {
+  static constexpr int W = 8;
+  static constexpr int SPLIT_PAGES = 64;
+};
+
+constexpr int kItemUnits = 4;   // units a work item can name
+constexpr int kItemInts = 8;    // int32 words per plan item: 4 units, the rotations, 3 unused
+constexpr int kMaxPairsPerUnit = 4;
+// Units a workgroup can finish together: the LDS holds the partials of
+// (units x G) <= 32 query-head rows per wave.
+__host__ __device__ constexpr int units_cap(int group) { return group <= 8 ? 4 : 2; }
+
 struct DecodeArgs {
   const uint16_t* kpool;
   const uint16_t* vpool;
@@ -76,16 +110,25 @@ struct DecodeArgs {
   int32_t group;
   int32_t stride;     // max_pages_per_seq
   int32_t s_max;      // splits per sequence the grid covers
+  int32_t ucap;       // units_cap(group)
+  int32_t num_items;  // work items in the grid
   float scale_log2;   // scale * log2(e)
-  // fused append (all NULL for a plain decode): the new token's K/V rows
-  // [B][Hkv][D] and their positions [B]
-  const uint16_t* k_new;
-  const uint16_t* v_new;
-  const int32_t* positions;
-  // optional launch plan: workgroup (item, KV head) takes the split
-  // plan[item] = b | s << 20; NULL = every (sequence, split) in split-major order
+  // optional launch plan: workgroup (item, KV head) runs the units of
+  // plan[item * kItemInts + 0..3] (b | s << 20, or -1 for none) with the
+  // rotations packed 4 bits per unit in plan[item * kItemInts + 4]; NULL =
+  // per sequence, its splits in consecutive groups of ucap
   const int32_t* plan;
 };
+
+// A launch plan carried by value in the kernel's arguments (the runtime
+// copies the arguments at launch, so the host array is free again when the
+// call returns); NW words: NW / kItemInts items.
+template <int NW>
+struct InlinePlan {
+  int32_t w[NW];
+};
+constexpr int kInlineSmall = 256;     // 32 items, 1 KiB of arguments
+constexpr int kInlineLarge = 2048;    // 256 items, 8 KiB
 
 struct AppendArgs {
   uint16_t* kpool;
@@ -131,6 +174,7 @@ __device__ __forceinline__ u32x4 ld_stream(const u32x4* p) {
   else return *p;
 }
 
+
 template <int D>
 struct PairBuf {
   u32x4 k[2][D / 32];   // QK A operands: MFMA j, k-step kk
@@ -138,20 +182,20 @@ struct PairBuf {
 };
 
 // ---------------------------------------------------------------- decode
-// Per-lane constants for streaming one split of one (sequence, KV head).
+// Per-lane constants of one wave's stream. Every unit of a work item belongs
+// to the same KV head, so the tile offsets are shared; the pair list is held
+// one pair per lane and read with readlane.
 template <int D>
-struct SplitCtx {
+struct StreamCtx {
   const uint16_t* kbase;   // K pool + KV head tile + this lane's offset
   const uint16_t* vbase;   // V pool + KV head tile + this lane's offset
   size_t page_elems;       // elements per physical page in each pool
-  int my_pid;              // lane i: physical page of the split's logical page i
-  int npages;              // pages in this split
-  int pair_tok0;           // first token of the split
-  int tok1;                // one past the split's last token
   bool k_second;           // this lane's K row lies in the pair's second page
   bool v_second;           // this lane's V tokens lie in the pair's second page
   float sl2;               // softmax scale * log2(e)
-  bf16x8 qf[D / 32];       // query group, MFMA B operand
+  int pa;                  // lane i: physical page of the first page of the wave's pair i
+  int pb;                  // lane i: of its second page (the first again when there is none)
+  int ptu;                 // lane i: (first token of pair i) / 32, shifted left 2, | its unit
 };
 
 // Running softmax state of one wave: head = lane % 16.
@@ -163,11 +207,23 @@ struct SoftmaxState {
 };
 
 template <int D>
-__device__ __forceinline__ void issue_pair(const SplitCtx<D>& c, PairBuf<D>& buf, int pr) {
+__device__ __forceinline__ void init_state(SoftmaxState<D>& st) {
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < D / 16; ++mt) st.acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+__device__ __forceinline__ int sel4(int i, int x0, int x1, int x2, int x3) {
+  return i == 0 ? x0 : (i == 1 ? x1 : (i == 2 ? x2 : x3));
+}
+
+template <int D>
+__device__ __forceinline__ void issue_pair(const StreamCtx<D>& c, PairBuf<D>& buf, int i) {
   constexpr int KK = D / 32;
   constexpr int MT = D / 16;
-  const int pa = __builtin_amdgcn_readlane(c.my_pid, 2 * pr);
-  const int pb = __builtin_amdgcn_readlane(c.my_pid, min(2 * pr + 1, c.npages - 1));  // a missing second page re-reads the first (all masked)
+  const int pa = __builtin_amdgcn_readlane(c.pa, i);
+  const int pb = __builtin_amdgcn_readlane(c.pb, i);
   const uint16_t* kp = c.kbase + (size_t)(c.k_second ? pb : pa) * c.page_elems;
   const uint16_t* vp = c.vbase + (size_t)(c.v_second ? pb : pa) * c.page_elems;
 #pragma unroll
@@ -181,19 +237,20 @@ __device__ __forceinline__ void issue_pair(const SplitCtx<D>& c, PairBuf<D>& buf
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// One page pair (tokens pair_tok .. pair_tok + 31; those at or past tok1 are
+// masked) into the running state.
 template <int D>
-__device__ __forceinline__ void compute_pair(const SplitCtx<D>& c, PairBuf<D>& buf, int pr,
-                                             SoftmaxState<D>& st, int grp) {
+__device__ __forceinline__ void compute_pair(const bf16x8 (&qf)[D / 32], float sl2, int pair_tok, int tok1,
+                                             PairBuf<D>& buf, SoftmaxState<D>& st, int grp) {
   constexpr int KK = D / 32;
   constexpr int MT = D / 16;
-  const int pair_tok = c.pair_tok0 + 2 * kPage * pr;
   f32x4 sc[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     sc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf.k[j][kk]), c.qf[kk], sc[j], 0, 0, 0);
+      sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf.k[j][kk]), qf[kk], sc[j], 0, 0, 0);
   }
   // scores in log2 units; tokens past the split end are masked by select
   const int t_lane = pair_tok + 8 * grp;
@@ -203,8 +260,8 @@ __device__ __forceinline__ void compute_pair(const SplitCtx<D>& c, PairBuf<D>& b
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float x = sc[j][i] * c.sl2;
-      x = (t_lane + 4 * j + i < c.tok1) ? x : -INFINITY;
+      float x = sc[j][i] * sl2;
+      x = (t_lane + 4 * j + i < tok1) ? x : -INFINITY;
       sv[4 * j + i] = x;
       mx = fmaxf(mx, x);
     }
@@ -229,8 +286,8 @@ __device__ __forceinline__ void compute_pair(const SplitCtx<D>& c, PairBuf<D>& b
     for (int mt = 0; mt < MT; ++mt) st.acc[mt] *= alpha;
   }
   // tail pair: zero V of masked tokens (0 * NaN would poison the product)
-  if (pair_tok + 2 * kPage > c.tok1) {
-    int cnt = c.tok1 - t_lane;
+  if (pair_tok + 2 * kPage > tok1) {
+    int cnt = tok1 - t_lane;
     cnt = cnt < 0 ? 0 : (cnt > 8 ? 8 : cnt);
     uint32_t keep[4];
 #pragma unroll
@@ -249,295 +306,98 @@ __device__ __forceinline__ void compute_pair(const SplitCtx<D>& c, PairBuf<D>& b
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Stream pairs first, first + step, ... (< npairs) of a split into st. The
-// next pair's loads are in flight while the current one is computed (two
-// register buffers). The steady-state loop issues unconditionally and the last
-// one or two pairs are peeled, so every wait for loaded data counts exactly
-// the loads issued after it and never waits for the prefetch.
+// LDS of the decode workgroup, in floats: the item's query rows (BF16), then
+// per (unit, logical wave) the partial max and sum of 16 heads, the partial
+// accumulators of (unit, logical wave, head) rows, and the units' merged
+// max and sum.
 template <int D>
-__device__ __forceinline__ void stream_pairs(const SplitCtx<D>& c, int first, int step, int npairs,
-                                             SoftmaxState<D>& st, int grp) {
-  const int my_n = first < npairs ? (npairs - first + step - 1) / step : 0;
-  if (my_n <= 0) return;
-  PairBuf<D> b0, b1;
-  issue_pair(c, b0, first);
-  int it = 0;
-  for (; it + 2 < my_n; it += 2) {
-    issue_pair(c, b1, first + (it + 1) * step);
-    compute_pair(c, b0, first + it * step, st, grp);
-    issue_pair(c, b0, first + (it + 2) * step);
-    compute_pair(c, b1, first + (it + 1) * step, st, grp);
-  }
-  if (it + 1 < my_n) {
-    issue_pair(c, b1, first + (it + 1) * step);
-    compute_pair(c, b0, first + it * step, st, grp);
-    compute_pair(c, b1, first + (it + 1) * step, st, grp);
-  } else {
-    compute_pair(c, b0, first + it * step, st, grp);
-  }
-}
+struct DecodeLds {
+  static constexpr int W = DecodeGeom<D>::W;
+  static constexpr int ROW = D + 4;                               // padded accumulator row
+  static constexpr int Q = 0;                                     // BF16 query rows [unit][16][D]
+  static constexpr int WM = Q + kItemUnits * 16 * D / 2;          // [unit][lw][16]
+  static constexpr int WL = WM + kItemUnits * W * 16;
+  static constexpr int ACC = WL + kItemUnits * W * 16;            // [(unit * W + lw) * G + head][ROW]
+  static constexpr int UM = ACC + 32 * W * ROW;                   // [unit][16]
+  static constexpr int UL = UM + kItemUnits * 16;
+  static constexpr int TOTAL = UL + kItemUnits * 16;
+};
 
-// Lane i's raw block-table entry for logical page s * SPLIT_PAGES + i (0 past
-// the row). Needs no context length, so it is loaded alongside it.
-template <int SPLIT_PAGES>
-__device__ __forceinline__ int load_split_pages(const DecodeArgs& a, int b, int s, int lane) {
-  const int p = s * SPLIT_PAGES + lane;
-  return (lane < SPLIT_PAGES && p < a.stride) ? a.block_tables[(size_t)b * a.stride + p] : 0;
-}
-
-template <int D, int SPLIT_PAGES>
-__device__ __forceinline__ void make_split_ctx(const DecodeArgs& a, int b, int kvh, int s, int n,
-                                               int lane, int raw_pid, SplitCtx<D>& c) {
-  constexpr int KK = D / 32;
-  constexpr int TILE = kPage * D;
-  constexpr int SPLIT_TOK = SPLIT_PAGES * kPage;
-  const int r = lane & 15;
-  const int grp = lane >> 4;
-  const int G = a.group;
-  const int tok0 = s * SPLIT_TOK;
-  c.tok1 = min(tok0 + SPLIT_TOK, n);
-  c.pair_tok0 = tok0;
-  const int p0 = tok0 / kPage;
-  c.npages = (c.tok1 - tok0 + kPage - 1) / kPage;
-  // this split's physical page ids, one per lane, clamped into the pool
-  (void)p0;
-  c.my_pid = lane < c.npages ? (raw_pid < 0 ? 0 : (raw_pid >= a.num_pages ? a.num_pages - 1 : raw_pid)) : 0;
-  // query group as the MFMA B operand (columns = heads, zero past G)
+// A wave's partial state of one unit (logical wave lw) into LDS slot
+// (unit * W + lw).
+template <int D>
+__device__ __forceinline__ void park_partial(float* smem, int slot, int G, const SoftmaxState<D>& st, int r,
+                                             int grp) {
+  using L = DecodeLds<D>;
+  float l = st.l + __shfl_xor(st.l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (grp == 0) {
+    smem[L::WM + slot * 16 + r] = st.m;
+    smem[L::WL + slot * 16 + r] = l;
+  }
   if (r < G) {
-    const uint16_t* qp = a.q + ((size_t)b * a.num_q_heads + (size_t)kvh * G + r) * D;
+    float* dst = smem + L::ACC + (size_t)(slot * G + r) * L::ROW + 4 * grp;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) c.qf[kk] = as_bf16x8(*(const u32x4*)(qp + kdim<D>(grp, kk)));
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) c.qf[kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    for (int mt = 0; mt < D / 16; ++mt) *(f32x4*)(dst + 16 * mt) = st.acc[mt];
   }
-  c.page_elems = (size_t)a.num_kv_heads * TILE;
-  const int koff = k_offset(8 * ((r >> 2) & 1) + (r & 3), kdim<D>(grp, 0));
-  const int voff = r * kPage + 8 * (grp & 1);
-  c.k_second = (r >> 3) != 0;
-  c.v_second = (grp >> 1) != 0;
-  c.kbase = a.kpool + (size_t)kvh * TILE + koff;
-  c.vbase = a.vpool + (size_t)kvh * TILE + voff;
-  c.sl2 = a.scale_log2;
 }
 
 template <int D>
-__device__ __forceinline__ void init_state(SoftmaxState<D>& st) {
-  st.m = -INFINITY;
-  st.l = 0.f;
+__device__ __forceinline__ void load_query(const float* smem, int u, int G, int r, int grp, bf16x8 (&qf)[D / 32]) {
+  const u32x4* sq = (const u32x4*)(smem + DecodeLds<D>::Q);
 #pragma unroll
-  for (int mt = 0; mt < D / 16; ++mt) st.acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kk = 0; kk < D / 32; ++kk)
+    qf[kk] = r < G ? as_bf16x8(sq[(u * 16 + r) * (D / 8) + grp + 4 * kk]) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
 }
 
-// Write one V column (the D values of one token) into a slot-minor V tile by
-// rewriting whole 32-byte slot rows: lane i handles rows i, i + 64, ...
+// The wave's pairs 0 .. T-1 (of all units in turn; pair 0 already issued
+// into b0). The next pair's loads are in flight while the current one is
+// computed (two register buffers), also across a unit boundary; at a
+// boundary the finished unit's state is parked in LDS. The steady-state loop issues unconditionally and the last one or
+// two pairs are peeled, so a wait for loaded data never covers the prefetch.
 template <int D>
-__device__ __forceinline__ void write_v_column(uint16_t* vtile, const uint16_t* vn, int slot, int lane) {
-  const int w = (slot & 7) >> 1;
-  const int half = slot >> 3;
-  const uint32_t sh = (slot & 1) * 16;
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i) {
-    const int dd = lane + 64 * i;
-    u32x4* row = (u32x4*)(vtile + (size_t)dd * kPage);
-    u32x4 h0 = row[0];
-    u32x4 h1 = row[1];
-    const uint32_t nv = vn[dd];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t upd0 = (h0[e] & ~(0xFFFFu << sh)) | (nv << sh);
-      const uint32_t upd1 = (h1[e] & ~(0xFFFFu << sh)) | (nv << sh);
-      h0[e] = (half == 0 && e == w) ? upd0 : h0[e];
-      h1[e] = (half == 1 && e == w) ? upd1 : h1[e];
-    }
-    row[0] = h0;
-    row[1] = h1;
-  }
-}
-
-// Fused append of a position the decode does not attend over (at or past the
-// context length): plain stores by wave 0 of the workgroup of the split the
-// position falls in; nothing in this launch reads that slot.
-template <int D>
-__device__ __forceinline__ void append_unattended(const DecodeArgs& a, int b, int kvh, int pos,
-                                                  int lane) {
-  const int pid = a.block_tables[(size_t)b * a.stride + pos / kPage];
-  if (pid < 0 || pid >= a.num_pages) return;
-  const int slot = pos % kPage;
-  const size_t tile = (size_t)pid * a.num_kv_heads + kvh;
-  const uint16_t* kn = a.k_new + ((size_t)b * a.num_kv_heads + kvh) * D;
-  const uint16_t* vn = a.v_new + ((size_t)b * a.num_kv_heads + kvh) * D;
-  uint16_t* ktile = const_cast<uint16_t*>(a.kpool) + tile * kPage * D;
-  uint16_t* vdst = const_cast<uint16_t*>(a.vpool) + tile * D * kPage + slot;
-  if (lane < D / 8) *(u32x4*)(ktile + k_offset(slot, 8 * lane)) = *(const u32x4*)(kn + 8 * lane);
-  write_v_column<D>(vdst - slot, vn, slot, lane);
-}
-
-// Fused append of an attended position, by the wave that will read its page
-// pair: every lane stores exactly the bytes of the new token that it loads
-// itself later (its chunks of the K row, its elements of the V column), so
-// program order within the lane makes its own later loads return them. No
-// other lane, wave or workgroup reads that slot in this launch, so no fence
-// or barrier is needed. pid is the token's page, p_in_pair 0/1 its page
-// within the pair, slot its slot.
-template <int D>
-__device__ __forceinline__ void append_by_reader(const DecodeArgs& a, int b, int kvh, int pid,
-                                                 int p_in_pair, int slot, int lane) {
-  constexpr int KK = D / 32;
-  constexpr int MT = D / 16;
-  const int r = lane & 15;
-  const int grp = lane >> 4;
-  const size_t tile = (size_t)pid * a.num_kv_heads + kvh;
-  const uint16_t* kn = a.k_new + ((size_t)b * a.num_kv_heads + kvh) * D;
-  const uint16_t* vn = a.v_new + ((size_t)b * a.num_kv_heads + kvh) * D;
-  // K: the QK row of this token is r = 8 * page-in-pair + 4 * (slot / 8) + slot % 4
-  if (r == 8 * p_in_pair + 4 * (slot >> 3) + (slot & 3)) {
-    uint16_t* ktile = const_cast<uint16_t*>(a.kpool) + tile * kPage * D;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      *(u32x4*)(ktile + k_offset(slot, kdim<D>(grp, kk))) = *(const u32x4*)(kn + kdim<D>(grp, kk));
-  }
-  // V: the two lane groups 2 * page-in-pair and 2 * page-in-pair + 1 load the
-  // two 16-byte halves of every 32-byte slot row of this page. They read their
-  // halves, put v_new into the token's element and write the halves back, so
-  // each row is written whole (a lone 2-byte write would make the memory side
-  // read-modify-write the sector).
-  if ((grp >> 1) == p_in_pair) {
-    const bool mine = (grp & 1) == (slot >> 3);
-    const int w = (slot & 7) >> 1;
-    const uint32_t sh = (slot & 1) * 16;
-    uint16_t* vrow = const_cast<uint16_t*>(a.vpool) + tile * D * kPage + r * kPage + 8 * (grp & 1);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      u32x4 h = *(const u32x4*)(vrow + mt * 16 * kPage);
-      const uint32_t nv = vn[16 * mt + r];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (mine && e == w) h[e] = (h[e] & ~(0xFFFFu << sh)) | (nv << sh);
-      *(u32x4*)(vrow + mt * 16 * kPage) = h;
-    }
-  }
-}
-
-// Waves per SIMD the register budget must allow (512 registers per lane).
-__host__ __device__ constexpr int occupancy(int d) { return d == 64 ? 4 : 2; }
-
-// Decode: one workgroup of W waves per (split, sequence, KV head); wave w
-// takes pairs w, w + W, ...; the waves merge through LDS. With FUSED the
-// launch also appends each sequence's new token (pa_decode_append).
-
-template <int D, int W, int SPLIT_PAGES, bool FUSED>
-__global__ __launch_bounds__(64 * W, occupancy(D)) void decode_split_kernel(DecodeArgs a) {
-  static_assert(D == 64 || D == 128, "head_dim");
-  static_assert(SPLIT_PAGES % 2 == 0 && SPLIT_PAGES <= 64, "split pages: even, at most one per lane");
-  constexpr int MT = D / 16;
-  constexpr int SPLIT_TOK = SPLIT_PAGES * kPage;
-  constexpr int LDS_ROW = D + 4;
-  extern __shared__ float smem[];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane & 15;
-  const int grp = lane >> 4;
-  const int wg = blockIdx.x;
-  const int kvh = wg % a.num_kv_heads;
-  const int rest = wg / a.num_kv_heads;
-  int b, s;
-  if (a.plan) {
-    const uint32_t item = (uint32_t)a.plan[rest];
-    b = (int)(item & 0xFFFFFu);
-    s = (int)(item >> 20);
-    if (b >= a.num_seqs || s >= a.s_max) return;
-  } else {
-    b = rest % a.num_seqs;
-    s = rest / a.num_seqs;
-  }
-  const int G = a.group;
-
-  // the independent loads of the prologue are issued together
-  int pos = FUSED ? a.positions[b] : -1;
-  const int raw_pid = load_split_pages<SPLIT_PAGES>(a, b, s, lane);
-  const int ctx_b = a.ctx[b];
-  const int n = clamp_ctx(ctx_b, a.stride);
-  if (FUSED && pos >= 0 && pos < a.stride * kPage && pos / SPLIT_TOK == s) {
-    if (pos >= n) {
-      if (wave == 0) append_unattended<D>(a, b, kvh, pos, lane);
-    } else {
-      const int lp = pos / kPage - s * SPLIT_PAGES;          // page within this split
-      if (wave == (lp >> 1) % W) {                           // the wave reading its pair
-        const int v = __builtin_amdgcn_readlane(raw_pid, lp);
-        if (v >= 0 && v < a.num_pages) append_by_reader<D>(a, b, kvh, v, lp & 1, pos % kPage, lane);
-      }
-    }
-  }
-  if (n == 0) {
-    if (s == 0) {
-      float* o = a.out + ((size_t)b * a.num_q_heads + (size_t)kvh * G) * D;
-      for (int e = threadIdx.x; e < G * D; e += 64 * W) o[e] = 0.f;
-    }
-    return;
-  }
-  const int nsplit = (n + SPLIT_TOK - 1) / SPLIT_TOK;
-  if (s >= nsplit) return;
-
-  SplitCtx<D> c;
-  make_split_ctx<D, SPLIT_PAGES>(a, b, kvh, s, n, lane, raw_pid, c);
+__device__ __forceinline__ void stream_item(const StreamCtx<D>& c, int T, PairBuf<D>& b0, float* smem, int G,
+                                            int r, int grp, int lw0, int lw1, int lw2, int lw3, int te0, int te1,
+                                            int te2, int te3) {
+  constexpr int W = DecodeGeom<D>::W;
+  if (T <= 0) return;
   SoftmaxState<D> st;
   init_state(st);
-  stream_pairs(c, wave, W, (c.npages + 1) >> 1, st, grp);
-  st.l += __shfl_xor(st.l, 16, 64);
-  st.l += __shfl_xor(st.l, 32, 64);
-
-  float* sm_m = smem;
-  float* sm_l = smem + W * 16;
-  float* sm_acc = smem + 2 * W * 16;
-  if (grp == 0) {
-    sm_m[wave * 16 + r] = st.m;
-    sm_l[wave * 16 + r] = st.l;
-  }
-  if (r < G) {
-    float* dst = sm_acc + (size_t)(wave * G + r) * LDS_ROW + 4 * grp;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) *(f32x4*)(dst + 16 * mt) = st.acc[mt];
-  }
-  // LDS-only fences: the barrier must not wait for global stores in flight
-  // (a fused append's pool writes)
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-
-  const bool alone = nsplit == 1;
-  const size_t head0 = (size_t)b * a.num_q_heads + (size_t)kvh * G;
-  for (int e = threadIdx.x; e < G * D; e += 64 * W) {
-    const int hh = e / D;
-    const int dd = e - hh * D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w * 16 + hh]);
-    float L = 0.f, A = 0.f;
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const float cw = __builtin_amdgcn_exp2f(sm_m[w * 16 + hh] - M);
-      L += cw * sm_l[w * 16 + hh];
-      A += cw * sm_acc[(size_t)(w * G + hh) * LDS_ROW + dd];
-    }
-    if (alone) {
-      a.out[(head0 + hh) * D + dd] = A / L;
-    } else {
-      const size_t slot = (head0 + hh) * a.s_max + s;
-      a.ws_acc[slot * D + dd] = A;
-      if (dd == 0) {
-        a.ws_ml[slot * 2] = M;
-        a.ws_ml[slot * 2 + 1] = L;
+  bf16x8 qf[D / 32];
+  int cur = -1;
+  int tok1 = 0;
+  auto step = [&](PairBuf<D>& buf, int i) {
+    const int tu = __builtin_amdgcn_readlane(c.ptu, i);
+    const int u = tu & 3;
+    if (u != cur) {
+      if (cur >= 0) {
+        park_partial<D>(smem, cur * W + sel4(cur, lw0, lw1, lw2, lw3), G, st, r, grp);
+        init_state(st);
       }
+      cur = u;
+      load_query<D>(smem, u, G, r, grp, qf);
+      tok1 = sel4(u, te0, te1, te2, te3);
     }
+    compute_pair<D>(qf, c.sl2, (tu >> 2) << 5, tok1, buf, st, grp);
+  };
+  PairBuf<D> b1;   // pair 0 is already in flight in b0
+  int it = 0;
+  for (; it + 2 < T; it += 2) {
+    issue_pair(c, b1, it + 1);
+    step(b0, it);
+    issue_pair(c, b0, it + 2);
+    step(b1, it + 1);
   }
+  if (it + 1 < T) {
+    issue_pair(c, b1, it + 1);
+    step(b0, it);
+    step(b1, it + 1);
+  } else {
+    step(b0, it);
+  }
+  park_partial<D>(smem, cur * W + sel4(cur, lw0, lw1, lw2, lw3), G, st, r, grp);
 }
 
-// One wave per (sequence, query head): combine the splits of sequences that
-// have more than one, in split order. Lane i holds split i's (m, l); they are
-// loaded together with the context length, so the partial outputs (read four
-// splits at a time) are two dependent loads away from the start.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -549,29 +409,16 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void merge_splits_kernel(DecodeArgs a, int split_tokens) {
+// Log-sum-exp merge of nsplit split partials of one (sequence, query head),
+// in split order, by one wave: ml(s) gives split s's (max in log2 units, sum),
+// acc(s, e) its unnormalised output element e. The decode workgroup (from
+// LDS) and the merge kernel (from the workspace) run this same code.
+template <int D, class ML, class ACC>
+__device__ __forceinline__ void lse_merge(int nsplit, int lane, ML ml, ACC acc, float* o) {
   constexpr int PER = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= a.num_seqs * a.num_q_heads) return;
-  const int b = item / a.num_q_heads;
-  const float* ml = a.ws_ml + (size_t)item * a.s_max * 2;
-  const float* acc = a.ws_acc + (size_t)item * a.s_max * D;
-  // the context length and the first 64 splits' (m, l) are loaded together;
-  // lanes past the sequence's split count drop theirs
-  const int ctx_b = a.ctx[b];
-  float m0 = -INFINITY, l0 = 0.f;
-  if (lane < a.s_max) {
-    m0 = ml[2 * lane];
-    l0 = ml[2 * lane + 1];
-  }
-  const int n = clamp_ctx(ctx_b, a.stride);
-  const int nsplit = (n + split_tokens - 1) / split_tokens;
-  if (nsplit <= 1) return;
-  float M = lane < nsplit ? m0 : -INFINITY;
-  for (int s0 = 64; s0 < nsplit; s0 += 64)
-    if (s0 + lane < nsplit) M = fmaxf(M, ml[2 * (s0 + lane)]);
+  float M = -INFINITY;
+  for (int s0 = 0; s0 < nsplit; s0 += 64)
+    if (s0 + lane < nsplit) M = fmaxf(M, ml(s0 + lane).x);
   M = wave_max(M);
   float L = 0.f;
   float A[PER];
@@ -581,36 +428,314 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(DecodeArgs a, int spl
     const int cnt = min(64, nsplit - s0);
     float c = 0.f;
     if (lane < cnt) {
-      const float mm = s0 == 0 ? m0 : ml[2 * (s0 + lane)];
-      const float ll = s0 == 0 ? l0 : ml[2 * (s0 + lane) + 1];
-      c = __builtin_amdgcn_exp2f(mm - M);
-      L += c * ll;
+      const float2 v = ml(s0 + lane);
+      c = __builtin_amdgcn_exp2f(v.x - M);
+      L = __builtin_fmaf(c, v.y, L);
     }
-    int j = 0;
-    for (; j + 4 <= cnt; j += 4) {
-      float v[4][PER];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int i = 0; i < PER; ++i) v[u][i] = acc[(size_t)(s0 + j + u) * D + lane + 64 * i];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float cu = __shfl(c, j + u, 64);
-#pragma unroll
-        for (int i = 0; i < PER; ++i) A[i] += cu * v[u][i];
-      }
-    }
-    for (; j < cnt; ++j) {
+#pragma unroll 4
+    for (int j = 0; j < cnt; ++j) {
       const float cu = __shfl(c, j, 64);
 #pragma unroll
-      for (int i = 0; i < PER; ++i) A[i] += cu * acc[(size_t)(s0 + j) * D + lane + 64 * i];
+      for (int i = 0; i < PER; ++i) A[i] = __builtin_fmaf(cu, acc(s0 + j, lane + 64 * i), A[i]);
     }
   }
   L = wave_sum(L);
   const float inv = 1.f / L;
-  float* o = a.out + (size_t)item * D;
 #pragma unroll
   for (int i = 0; i < PER; ++i) o[lane + 64 * i] = A[i] * inv;
+}
+
+// Waves per SIMD the register budget must allow (512 registers per lane).
+__host__ __device__ constexpr int occupancy(int d) { return d == 64 ? 4 : 2; }
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * DecodeGeom<D>::W, occupancy(D)) void decode_kernel(DecodeArgs a,
+                                                                                   InlinePlan<NW> ip) {
+  static_assert(D == 64 || D == 128, "head_dim");
+  constexpr int W = DecodeGeom<D>::W;
+  constexpr int SP = DecodeGeom<D>::SPLIT_PAGES;
+  constexpr int SPLIT_TOK = SP * kPage;
+  constexpr int TILE = kPage * D;
+  static_assert(SP / 2 <= kMaxPairsPerUnit * W, "at most 4 pairs per logical wave");
+  static_assert((W & (W - 1)) == 0 && W <= 16, "W: a power of two, rotations in 4 bits");
+  using L = DecodeLds<D>;
+  __shared__ __align__(16) float smem[L::TOTAL];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15;
+  const int grp = lane >> 4;
+  const int Hkv = a.num_kv_heads;
+  // grid: x = KV head, (y, z) = work item; linear workgroup order is KV head
+  // fastest, so with 8 KV heads each XCD takes one head of every item
+  const int kvh = blockIdx.x;
+  const int item = blockIdx.z * 65535 + blockIdx.y;
+  constexpr bool kInline = NW > kItemInts;
+  // only a grid past 65535 items has a ragged end; an inline plan holds at
+  // most 256 items, so its grid is exact
+  if constexpr (!kInline) {
+    if (item >= a.num_items) return;
+  }
+  const int G = a.group;
+  const int Hq = a.num_q_heads;
+  const int ucap = a.ucap;
+
+  // the item's units (sequence -1: none) and their rotations. The variants
+  // with an inline plan (NW > one item) read it from the kernel's arguments,
+  // together with the other arguments, in the first round of loads.
+  const int32_t* ctxp = a.ctx;
+  const int32_t* btp = a.block_tables;
+  const uint16_t* qp = a.q;
+  const int num_seqs = a.num_seqs;
+  const int s_max = a.s_max;
+  const int stride = a.stride;
+  int ub[kItemUnits], us[kItemUnits];
+  int rot = 0;
+  if (kInline || a.plan) {
+    int it[kItemUnits + 1];
+    if (kInline) {
+#pragma unroll
+      for (int k = 0; k <= kItemUnits; ++k) it[k] = ip.w[item * kItemInts + k];
+    } else {
+#pragma unroll
+      for (int k = 0; k <= kItemUnits; ++k) it[k] = a.plan[(size_t)item * kItemInts + k];
+    }
+    // every argument the next round of loads needs, in registers together
+    asm volatile("" ::"s"(it[0]), "s"(it[1]), "s"(it[2]), "s"(it[3]), "s"(it[4]), "s"(ctxp), "s"(btp), "s"(qp),
+                 "s"(num_seqs), "s"(s_max), "s"(stride));
+#pragma unroll
+    for (int u = 0; u < kItemUnits; ++u) {
+      const int e = it[u];
+      const int b = e & 0xFFFFF;
+      const int s = (int)((uint32_t)e >> 20);
+      const bool ok = u < ucap && e >= 0 && b < num_seqs && s < s_max;
+      ub[u] = ok ? b : -1;
+      us[u] = ok ? s : 0;
+    }
+    rot = it[kItemUnits];
+  } else {
+    const int b = item % num_seqs;
+    const int j = item / num_seqs;
+#pragma unroll
+    for (int u = 0; u < kItemUnits; ++u) {
+      const int s = j * ucap + u;
+      ub[u] = (u < ucap && s < s_max) ? b : -1;
+      us[u] = s;
+    }
+  }
+  if (ub[0] < 0 && ub[1] < 0 && ub[2] < 0 && ub[3] < 0) return;
+
+  // the second round, issued together and unconditionally (absent units read
+  // sequence 0, whose row always exists, and are masked after): the context
+  // lengths, this lane's block-table entry, this thread's query chunks
+  int raw_n[kItemUnits];
+  {
+    // the context lengths do not change during a launch: scalar loads
+    // through the constant address space
+    typedef __attribute__((address_space(4))) const int32_t cint;
+    const cint* cctx = (const cint*)ctxp;
+#pragma unroll
+    for (int u = 0; u < kItemUnits; ++u) raw_n[u] = cctx[max(ub[u], 0)];
+  }
+  // lane t < 32: page j = t % 2 of pair k = (t / 2) % 4 of unit t / 8
+  const int tu = (lane >> 3) & 3;
+  const int tk = (lane >> 1) & 3;
+  const int tj = lane & 1;
+  const int t_b = sel4(tu, ub[0], ub[1], ub[2], ub[3]);
+  const int t_lw = (wave - ((rot >> (4 * tu)) & 15)) & (W - 1);
+  const int t_pi = 2 * (t_lw + W * tk) + tj;                                 // page within the split
+  const int t_lp = sel4(tu, us[0], us[1], us[2], us[3]) * SP + t_pi;        // logical page
+  const bool t_ok = lane < 32 && t_b >= 0 && t_lp < stride;
+  int raw = btp[t_ok ? (size_t)t_b * stride + t_lp : 0];
+  // query rows: 16-byte chunk t = (unit * 16 + head) * (D / 8) + c of the
+  // LDS copy, thread threadIdx.x + i * 64 * W for i < QCH
+  constexpr int QCHUNKS = kItemUnits * 16 * (D / 8);
+  constexpr int QCH = (QCHUNKS + 64 * W - 1) / (64 * W);
+  u32x4 qv[QCH];
+  bool qok[QCH];
+#pragma unroll
+  for (int i = 0; i < QCH; ++i) {
+    const int t = threadIdx.x + i * 64 * W;
+    const int u = (t / (16 * (D / 8))) & 3;
+    const int h = (t / (D / 8)) & 15;
+    const int ch = t % (D / 8);
+    const int b = sel4(u, ub[0], ub[1], ub[2], ub[3]);
+    qok[i] = t < QCHUNKS && b >= 0 && h < G;
+    qv[i] = *(const u32x4*)(qp + ((size_t)(qok[i] ? b : 0) * Hq + (size_t)kvh * G + (qok[i] ? h : 0)) * D + 8 * ch);
+  }
+  raw &= -(int)t_ok;
+  int n[kItemUnits];
+#pragma unroll
+  for (int u = 0; u < kItemUnits; ++u) n[u] = clamp_ctx(raw_n[u], stride) & -(int)(ub[u] >= 0);
+
+  // per unit: tokens, pages, pairs; this wave's logical wave and its pairs
+  int nsplit[kItemUnits], te[kItemUnits], np[kItemUnits], lw[kItemUnits], cnt[kItemUnits];
+#pragma unroll
+  for (int u = 0; u < kItemUnits; ++u) {
+    nsplit[u] = (n[u] + SPLIT_TOK - 1) / SPLIT_TOK;
+    const bool live = ub[u] >= 0 && us[u] < nsplit[u];
+    const int tok0 = us[u] * SPLIT_TOK;
+    te[u] = live ? min(tok0 + SPLIT_TOK, n[u]) : 0;
+    np[u] = live ? (te[u] - tok0 + kPage - 1) / kPage : 0;
+    const int npairs = (np[u] + 1) >> 1;
+    lw[u] = (wave - ((rot >> (4 * u)) & 15)) & (W - 1);
+    cnt[u] = npairs > lw[u] ? (npairs - lw[u] + W - 1) / W : 0;
+  }
+  // page ids: clamped into the pool; a pair's missing second page re-reads
+  // its first (all its tokens are masked)
+  int pid = raw < 0 ? 0 : (raw >= a.num_pages ? a.num_pages - 1 : raw);
+  const int first = __shfl(pid, lane & ~1, 64);
+  pid = t_pi < sel4(tu, np[0], np[1], np[2], np[3]) ? pid : first;
+  // the wave's pairs in stream order: lane f holds pair f
+  const int F1 = cnt[0], F2 = F1 + cnt[1], F3 = F2 + cnt[2], T = F3 + cnt[3];
+  const int fu = (lane >= F1) + (lane >= F2) + (lane >= F3);
+  const int fk = lane - sel4(fu, 0, F1, F2, F3);
+  const int src = (lane < T) ? 8 * fu + 2 * fk : 0;
+  StreamCtx<D> c;
+  c.pa = __shfl(pid, src, 64);
+  c.pb = __shfl(pid, src + 1, 64);
+  {
+    const int ptok = sel4(fu, us[0], us[1], us[2], us[3]) * SPLIT_TOK +
+                     2 * kPage * (sel4(fu, lw[0], lw[1], lw[2], lw[3]) + W * fk);
+    c.ptu = ((ptok >> 5) << 2) | fu;
+  }
+  c.page_elems = (size_t)Hkv * TILE;
+  c.k_second = (r >> 3) != 0;
+  c.v_second = (grp >> 1) != 0;
+  c.kbase = a.kpool + (size_t)kvh * TILE + k_offset(8 * ((r >> 2) & 1) + (r & 3), kdim<D>(grp, 0));
+  c.vbase = a.vpool + (size_t)kvh * TILE + r * kPage + 8 * (grp & 1);
+  c.sl2 = a.scale_log2;
+
+  // pair 0's loads go out before the barrier that publishes the query rows
+  // in LDS (LDS-only fences: the barrier does not wait for them)
+  // (unconditional, so that the wait for the query rows below counts these
+  // loads; a wave without pairs reads its lane 0 page, a valid one, for nothing)
+  PairBuf<D> b0;
+  issue_pair(c, b0, 0);
+  {
+    u32x4* sq = (u32x4*)(smem + L::Q);
+#pragma unroll
+    for (int i = 0; i < QCH; ++i) {
+      const int t = threadIdx.x + i * 64 * W;
+      const uint32_t m = -(uint32_t)qok[i];
+      if (t < QCHUNKS) sq[t] = u32x4{qv[i][0] & m, qv[i][1] & m, qv[i][2] & m, qv[i][3] & m};
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+
+  // units this wave has no pair of still get their (empty) partial
+#pragma unroll
+  for (int u = 0; u < kItemUnits; ++u) {
+    if (np[u] > 0 && cnt[u] == 0) {
+      SoftmaxState<D> e;
+      init_state(e);
+      park_partial<D>(smem, u * W + lw[u], G, e, r, grp);
+    }
+  }
+  stream_item<D>(c, T, b0, smem, G, r, grp, lw[0], lw[1], lw[2], lw[3], te[0], te[1], te[2], te[3]);
+
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+
+  // sequences whose splits (2 .. ucap of them) all lie in this item, in
+  // split order from unit u0: finished here
+  bool whole[kItemUnits];
+  bool any_whole = false;
+#pragma unroll
+  for (int u0 = 0; u0 < kItemUnits; ++u0) {
+    const int ns = nsplit[u0];
+    bool ok = ub[u0] >= 0 && us[u0] == 0 && ns >= 2 && ns <= ucap && u0 + ns <= kItemUnits;
+#pragma unroll
+    for (int v = 1; v < kItemUnits; ++v) {
+      const int uv = u0 + v < kItemUnits ? u0 + v : kItemUnits - 1;
+      if (v < ns) ok = ok && u0 + v < kItemUnits && ub[uv] == ub[u0] && us[uv] == v;
+    }
+    whole[u0] = ok;
+    any_whole = any_whole || ok;
+  }
+
+  // merge each unit's W partials in logical-wave order
+  const size_t head_kv = (size_t)kvh * G;
+  for (int e = threadIdx.x; e < kItemUnits * G * D; e += 64 * W) {
+    const int u = e / (G * D);
+    const int rem = e - u * G * D;
+    const int hh = rem / D;
+    const int dd = rem - hh * D;
+    const int b = sel4(u, ub[0], ub[1], ub[2], ub[3]);
+    if (b < 0) continue;
+    const int s = sel4(u, us[0], us[1], us[2], us[3]);
+    const int nn = sel4(u, n[0], n[1], n[2], n[3]);
+    const int ns = sel4(u, nsplit[0], nsplit[1], nsplit[2], nsplit[3]);
+    const size_t head = (size_t)b * Hq + head_kv + hh;
+    if (nn == 0) {
+      if (s == 0) a.out[head * D + dd] = 0.f;
+      continue;
+    }
+    if (s >= ns) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, smem[L::WM + (u * W + w) * 16 + hh]);
+    float Ls = 0.f, A = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float cw = __builtin_amdgcn_exp2f(smem[L::WM + (u * W + w) * 16 + hh] - M);
+      Ls += cw * smem[L::WL + (u * W + w) * 16 + hh];
+      A += cw * smem[L::ACC + (size_t)((u * W + w) * G + hh) * L::ROW + dd];
+    }
+    if (ns == 1) {
+      a.out[head * D + dd] = A / Ls;
+    } else if (ns <= ucap) {
+      smem[L::ACC + (size_t)((u * W) * G + hh) * L::ROW + dd] = A;   // this thread's own element
+      if (dd == 0) {
+        smem[L::UM + u * 16 + hh] = M;
+        smem[L::UL + u * 16 + hh] = Ls;
+      }
+    } else {
+      const size_t slot = head * a.s_max + s;
+      a.ws_acc[slot * D + dd] = A;
+      if (dd == 0) {
+        a.ws_ml[slot * 2] = M;
+        a.ws_ml[slot * 2 + 1] = Ls;
+      }
+    }
+  }
+  if (!any_whole) return;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+#pragma unroll
+  for (int u0 = 0; u0 < kItemUnits; ++u0) {
+    if (!whole[u0]) continue;
+    for (int hh = wave; hh < G; hh += W) {
+      auto ml = [&](int s) {
+        return make_float2(smem[L::UM + (u0 + s) * 16 + hh], smem[L::UL + (u0 + s) * 16 + hh]);
+      };
+      auto acc = [&](int s, int e) { return smem[L::ACC + (size_t)(((u0 + s) * W) * G + hh) * L::ROW + e]; };
+      lse_merge<D>(nsplit[u0], lane, ml, acc, a.out + ((size_t)ub[u0] * Hq + head_kv + hh) * D);
+    }
+  }
+}
+
+// One wave per (sequence, query head) of the sequences with more splits than
+// a work item holds: their split partials, merged in split order.
+template <int D>
+__global__ __launch_bounds__(256) void merge_splits_kernel(DecodeArgs a) {
+  constexpr int SPLIT_TOK = DecodeGeom<D>::SPLIT_PAGES * kPage;
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= a.num_seqs * a.num_q_heads) return;
+  const int b = item / a.num_q_heads;
+  const int n = clamp_ctx(a.ctx[b], a.stride);
+  const int nsplit = (n + SPLIT_TOK - 1) / SPLIT_TOK;
+  if (nsplit <= a.ucap) return;
+  const float* ml = a.ws_ml + (size_t)item * a.s_max * 2;
+  const float* acc = a.ws_acc + (size_t)item * a.s_max * D;
+  lse_merge<D>(
+      nsplit, lane, [&](int s) { return make_float2(ml[2 * s], ml[2 * s + 1]); },
+      [&](int s, int e) { return acc[(size_t)s * D + e]; }, a.out + (size_t)item * D);
 }
 
 // ---------------------------------------------------------------- append

@@ -1,11 +1,15 @@
 /*
  * abi_fuzz.c - the host-side code of libpakv (pakv.hip compiled for the
  * host only) under AddressSanitizer and UBSan (tests/test_abi_sanitized.py):
- *   - pa_decode_plan on random context lengths, block-table widths and head
- *     dims, into plan buffers of exactly the stated capacity: every existing
- *     (sequence, split) appears once (an empty context once, as split 0),
- *     page counts never increase along the plan outside the reversed tiers
- *     of a one-round grid, and a capacity one short is refused untouched;
+ *   - pa_decode_plan on random context lengths, block-table widths, head
+ *     dims and group sizes: whole items of 8 words, each with 1 .. ucap
+ *     units (4, or 2 when more than 8 query heads share a KV head); every
+ *     existing (sequence, split) exactly once (an empty context once, as
+ *     split 0); a sequence with 2 .. ucap splits whole, in split order, in one
+ *     item; each unit's rotation the pairs before it in its item mod the
+ *     workgroup's waves; items by pairs, largest first; and the same call
+ *     into a buffer one word short of the plan refused, nothing written past
+ *     it;
  *   - pa_prefill_plan on random cache and chunk lengths (negative and past
  *     the bounds included): every row block that holds rows appears once
  *     and no other, costs never increase along the plan outside the
@@ -42,9 +46,18 @@ static void fail(const char* what, long round) {
 #define DEV ((void*)(uintptr_t)0x100000)
 #define DEV_MIS ((void*)(uintptr_t)0x100002)
 
+static int64_t clamp_ctx64(int32_t c, int32_t stride) {
+  int64_t n = c < 0 ? 0 : c;
+  return n > (int64_t)stride * 16 ? (int64_t)stride * 16 : n;
+}
+
 static void plan_round(long round) {
   const int d = rnd(2) ? 64 : 128;
   const int hkv = 1 + (int)rnd(8);
+  const int group = 1 + (int)rnd(16);
+  const int hq = hkv * group;
+  const int ucap = group <= 8 ? 4 : 2;
+  const int waves = d == 64 ? 16 : 8;
   pa_pool* pool = NULL;
   if (pa_pool_create(&pool, DEV, DEV, 1 + (int)rnd(100000), 16, hkv, d) != PA_OK) fail("pool", round);
   const int32_t num_seqs = (int32_t)rnd(300);
@@ -59,49 +72,71 @@ static void plan_round(long round) {
                                                               : (int32_t)rnd((uint32_t)stride * 16 + 1);
   }
   const int split_tok = pa_split_tokens(d);
-  if (split_tok <= 0 || split_tok % 32 != 0) fail("split tokens", round);
+  if (split_tok != (d == 64 ? 2048 : 1024)) fail("split tokens", round);
   const int sp = split_tok / 16;
-  /* the exact item count */
-  int64_t need = 0;
+  int64_t units = 0;
   for (int b = 0; b < num_seqs; ++b) {
-    int64_t n = ctx[b] < 0 ? 0 : ctx[b];
-    if (n > (int64_t)stride * 16) n = (int64_t)stride * 16;
-    const int64_t pages = (n + 15) / 16;
-    need += pages == 0 ? 1 : (pages + sp - 1) / sp;
+    const int64_t pages = (clamp_ctx64(ctx[b], stride) + 15) / 16;
+    units += pages == 0 ? 1 : (pages + sp - 1) / sp;
   }
-  if (need > cap) fail("need above capacity", round);
-  int32_t* plan = (int32_t*)malloc(sizeof(int32_t) * (size_t)(need ? need : 1));
+  if (units * 8 > cap) fail("units above capacity", round);
+  int32_t* plan = (int32_t*)malloc(sizeof(int32_t) * (size_t)(cap ? cap : 1));
   if (!plan) fail("oom", round);
-  int32_t items = -1;
-  if (num_seqs > 0 && need > 0) {
-    /* one short: refused, nothing written past the buffer (ASan watches) */
-    if (pa_decode_plan(pool, ctx, num_seqs, stride, plan, need - 1, &items) == PA_OK) fail("short capacity", round);
+  int32_t words = -1;
+  if (pa_decode_plan(pool, ctx, num_seqs, hq, stride, plan, cap, &words) != PA_OK) fail("plan", round);
+  if (num_seqs == 0) {
+    if (words != 0) fail("empty plan", round);
+  } else {
+    if (words <= 0 || words % 8 != 0 || words > units * 8) fail("word count", round);
+    /* one word short: refused, nothing written past the buffer (ASan watches) */
+    int32_t* short_buf = (int32_t*)malloc(sizeof(int32_t) * (size_t)(words - 1 ? words - 1 : 1));
+    if (!short_buf) fail("oom", round);
+    int32_t w2 = -1;
+    if (pa_decode_plan(pool, ctx, num_seqs, hq, stride, short_buf, words - 1, &w2) == PA_OK) fail("short capacity", round);
+    free(short_buf);
   }
-  if (pa_decode_plan(pool, ctx, num_seqs, stride, plan, need, &items) != PA_OK) fail("plan", round);
-  if (items != (num_seqs ? need : 0)) fail("item count", round);
-  /* every (sequence, split) once */
   char* seen = (char*)calloc((size_t)(num_seqs ? num_seqs : 1) * 2048, 1);
   if (!seen) fail("oom", round);
-  int64_t prev_pages = INT64_MAX;
-  int order_breaks = 0;
-  for (int32_t i = 0; i < items; ++i) {
-    const uint32_t it = (uint32_t)plan[i];
-    const int b = (int)(it & 0xFFFFFu);
-    const int s = (int)(it >> 20);
-    if (b >= num_seqs || s >= 2048) fail("item out of range", round);
-    if (seen[(size_t)b * 2048 + s]++) fail("item twice", round);
-    int64_t n = ctx[b] < 0 ? 0 : ctx[b];
-    if (n > (int64_t)stride * 16) n = (int64_t)stride * 16;
-    const int64_t pages = (n + 15) / 16;
-    const int64_t ns = pages == 0 ? 1 : (pages + sp - 1) / sp;
-    if (s >= ns) fail("split past the context", round);
-    const int64_t pg = pages == 0 ? 0 : (pages - (int64_t)s * sp < sp ? pages - (int64_t)s * sp : sp);
-    if (pg > prev_pages) ++order_breaks;
-    prev_pages = pg;
+  int64_t prev_pairs = INT64_MAX;
+  int64_t placed = 0;
+  for (int32_t i = 0; i < words; i += 8) {
+    const int32_t* it = plan + i;
+    if (it[5] != 0 || it[6] != 0 || it[7] != 0) fail("unused words", round);
+    int nu = 0;
+    int64_t before = 0, pairs_item = 0;
+    for (int u = 0; u < 4; ++u) {
+      if (it[u] < 0) {
+        for (int v = u; v < 4; ++v)
+          if (it[v] != -1) fail("unit after a gap", round);
+        break;
+      }
+      ++nu;
+      const int b = (int)((uint32_t)it[u] & 0xFFFFFu);
+      const int s = (int)((uint32_t)it[u] >> 20);
+      if (b >= num_seqs || s >= 2048) fail("unit out of range", round);
+      if (seen[(size_t)b * 2048 + s]++) fail("unit twice", round);
+      ++placed;
+      const int64_t pages = (clamp_ctx64(ctx[b], stride) + 15) / 16;
+      const int64_t ns = pages == 0 ? 1 : (pages + sp - 1) / sp;
+      if (s >= ns) fail("split past the context", round);
+      if (((uint32_t)it[4] >> (4 * u) & 15u) != (uint32_t)(before % waves)) fail("rotation", round);
+      const int64_t pg = pages == 0 ? 0 : (pages - (int64_t)s * sp < sp ? pages - (int64_t)s * sp : sp);
+      before += (pg + 1) / 2;
+      pairs_item += (pg + 1) / 2;
+      if (s == 0 && ns >= 2 && ns <= ucap) {   /* a short sequence: whole, in order, from here */
+        if (u + ns > 4) fail("short sequence cut", round);
+        for (int v = 1; v < ns; ++v)
+          if (it[u + v] != (int32_t)((uint32_t)b | ((uint32_t)v << 20))) fail("short sequence cut", round);
+      }
+      if (s > 0 && ns <= ucap && (u == 0 || it[u - 1] != (int32_t)((uint32_t)b | ((uint32_t)(s - 1) << 20))))
+        fail("split of a short sequence out of place", round);
+    }
+    if (nu == 0 || nu > ucap) fail("units per item", round);
+    if ((uint32_t)it[4] >> (4 * nu) != 0u) fail("rotation bits past the units", round);
+    if (pairs_item > prev_pairs) fail("item order", round);
+    prev_pairs = pairs_item;
   }
-  /* order: largest first, except for the reversed tiers of a one-round grid
-     (256 CUs x 4 decode workgroups per CU at d = 64, 2 at d = 128) */
-  if (order_breaks > 0 && (int64_t)items * hkv > 256 * (d == 64 ? 4 : 2)) fail("plan order", round);
+  if (placed != (num_seqs ? units : 0)) fail("units missing", round);
   free(seen);
   free(plan);
   free(ctx);
@@ -187,7 +222,8 @@ static void validation_round(long round) {
       if (pa_decode(pool, DEV_MIS, 4, 32, DEV, 4, DEV, 0.1f, out, NULL, 0, NULL) != PA_ERR_ALIGN) fail("decode align", round);
       break;
     case 2:
-      if (pa_decode(pool, DEV, 4, 32, DEV, 200, DEV, 0.1f, out, NULL, 0, NULL) != PA_ERR_WORKSPACE) fail("decode workspace", round);
+      /* 600 pages: more splits than a workgroup finishes, at either head_dim */
+      if (pa_decode(pool, DEV, 4, 32, DEV, 600, DEV, 0.1f, out, NULL, 0, NULL) != PA_ERR_WORKSPACE) fail("decode workspace", round);
       break;
     case 3:
       if (pa_decode(pool, DEV, 4, 32, DEV, 4, DEV, INFINITY, out, NULL, 0, NULL) != PA_ERR_INVALID) fail("decode scale", round);
@@ -196,7 +232,8 @@ static void validation_round(long round) {
       if (pa_decode_planned(pool, DEV, 4, 32, DEV, 4, DEV, 0.1f, out, NULL, 0, NULL, 1, NULL) != PA_ERR_NULL) fail("planned", round);
       break;
     case 5:
-      if (pa_decode_planned(pool, DEV, 4, 32, DEV, 4, DEV, 0.1f, out, NULL, 0, DEV, -1, NULL) != PA_ERR_INVALID) fail("planned items", round);
+      if (pa_decode_planned(pool, DEV, 4, 32, DEV, 4, DEV, 0.1f, out, NULL, 0, DEV, -8, NULL) != PA_ERR_INVALID) fail("planned items", round);
+      if (pa_decode_planned(pool, DEV, 4, 32, DEV, 4, DEV, 0.1f, out, NULL, 0, DEV, 12, NULL) != PA_ERR_INVALID) fail("planned whole items", round);
       break;
     case 6:
       if (pa_decode_append(pool, DEV, NULL, DEV, DEV, 4, 32, DEV, 4, DEV, 0.1f, out, NULL, 0, NULL) != PA_ERR_NULL) fail("append", round);
@@ -237,7 +274,7 @@ int main(int argc, char** argv) {
   }
   if (pa_decode_plan_capacity(NULL, 1, 1) >= 0) fail("capacity NULL", -1);
   int32_t items = 0;
-  if (pa_decode_plan(NULL, NULL, 0, 1, NULL, 0, &items) != PA_ERR_NULL) fail("plan NULL", -1);
+  if (pa_decode_plan(NULL, NULL, 0, 32, 1, NULL, 0, &items) != PA_ERR_NULL) fail("plan NULL", -1);
   for (long r = 0; r < rounds; ++r) {
     plan_round(r);
     prefill_plan_round(r);

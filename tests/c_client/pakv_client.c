@@ -250,7 +250,7 @@ int main(int argc, char** argv) {
     snprintf(name, sizeof name, "ctx_step%d.bin", s);
     write_file(name, ctx_host, (size_t)MB * 4);
     int32_t items = 0;
-    check(pa_decode_plan(pool, ctx_host, MB, stride, plan, plan_cap, &items), "pa_decode_plan");
+    check(pa_decode_plan(pool, ctx_host, MB, Hq, stride, plan, plan_cap, &items), "pa_decode_plan");
     upload(plan_dev, plan, (size_t)(items > 0 ? items : 1) * 4);
     for (int l = 0; l < L; ++l) {
       for (size_t e = 0; e < bt_layer; ++e) bt_clean[e] = bt_host[l * bt_layer + e] < 0 ? 0 : bt_host[l * bt_layer + e];

@@ -74,13 +74,18 @@ class Uploaded:
 
     def step(self, layers=None, fused=True, planned=False):
         """One decode step: per layer, append (when the workload appends) then
-        decode; fused=True uses the single-launch pa_decode_append, planned=True
-        (with fused=False) pa_decode_planned with the host-made launch plan."""
+        decode; fused=True uses the single-call pa_decode_append; planned (with
+        fused=False) drives decode with the host-made launch plan: "host" (the
+        plan in the kernel's arguments, pa_decode_planned_host, as the
+        benchmark runs it) or True / "device" (pa_decode_planned)."""
         import torch
         w = self.w
         plan = None
+        plan_host = None
         if planned:
-            plan = torch.from_numpy(B.decode_plan(self.pool, w.ctx_lens, w.stride)).to(self.dev)
+            plan_host = B.decode_plan(self.pool, w.ctx_lens, w.num_q_heads, w.stride)
+            if planned != "host":
+                plan = torch.from_numpy(plan_host).to(self.dev)
         for layer in (range(w.num_layers) if layers is None else layers):
             if w.append and fused:
                 B.decode_append(self.pool, self.q[layer], self.k_new[layer], self.v_new[layer],
@@ -92,6 +97,10 @@ class Uploaded:
             if plan is not None:
                 B.decode_planned(self.pool, self.q[layer], self.bt[layer], self.ctx, float(w.scale), plan,
                                  out=self.out[layer], workspace=self.workspace)
+                continue
+            if plan_host is not None:
+                B.decode_planned_host(self.pool, self.q[layer], self.bt[layer], self.ctx, float(w.scale),
+                                      plan_host, out=self.out[layer], workspace=self.workspace)
                 continue
             B.decode(self.pool, self.q[layer], self.bt[layer], self.ctx, float(w.scale),
                      out=self.out[layer], workspace=self.workspace)

@@ -61,7 +61,7 @@ def test_decode_validation():
     L = B.lib()
     pool = make_pool()
     f = lambda **kw: L.pa_decode(kw.get("pool", pool), kw.get("q", P), kw.get("B", 4), kw.get("Hq", 32),
-                                 kw.get("bt", P), kw.get("stride", 128), kw.get("ctx", P),
+                                 kw.get("bt", P), kw.get("stride", 600), kw.get("ctx", P),
                                  kw.get("scale", 0.125), kw.get("out", P), kw.get("ws", P),
                                  kw.get("ws_bytes", 1 << 30), None)
     assert f(pool=None) == NULL
@@ -76,11 +76,12 @@ def test_decode_validation():
     assert f(stride=0) == INVALID
     assert f(scale=float("inf")) == INVALID
     assert f(scale=float("nan")) == INVALID
+    assert f(scale=3.0e38) == INVALID          # scale * log2(e) overflows FP32
     assert f(q=MIS) == ALIGN
     assert f(out=MIS) == ALIGN
     assert f(ctx=MIS + 1) == ALIGN
-    assert f(ws=0) == WORKSPACE
-    need = L.pa_decode_workspace_bytes(pool, 4, 32, 128)
+    assert f(ws=0) == WORKSPACE                # 600 pages: 5 splits, more than a workgroup finishes
+    need = L.pa_decode_workspace_bytes(pool, 4, 32, 600)
     assert need > 0
     assert f(ws_bytes=need - 1) == WORKSPACE
     assert f(ws=MIS, ws_bytes=need) == ALIGN
@@ -93,7 +94,7 @@ def test_decode_append_validation():
     pool = make_pool()
     f = lambda **kw: L.pa_decode_append(kw.get("pool", pool), kw.get("q", P), kw.get("k", P),
                                         kw.get("v", P), kw.get("pos", P), kw.get("B", 4),
-                                        kw.get("Hq", 32), kw.get("bt", P), kw.get("stride", 128),
+                                        kw.get("Hq", 32), kw.get("bt", P), kw.get("stride", 600),
                                         kw.get("ctx", P), kw.get("scale", 0.125), kw.get("out", P),
                                         kw.get("ws", P), kw.get("ws_bytes", 1 << 30), None)
     assert f(pool=None) == NULL
@@ -111,16 +112,21 @@ def test_decode_append_validation():
 
 def test_workspace_sizes():
     L = B.lib()
-    pool = make_pool()
+    pool = make_pool()                        # 8 KV heads, d = 64
     split = L.pa_split_tokens(64)
-    assert split > 0 and split % 32 == 0
+    assert split == 2048 and L.pa_split_tokens(128) == 1024
     assert L.pa_split_tokens(80) == 0
     pages_one_split = split // 16
-    assert L.pa_decode_workspace_bytes(pool, 8, 32, pages_one_split) == 0
-    n = L.pa_decode_workspace_bytes(pool, 8, 32, pages_one_split + 1)
-    assert n >= 8 * 32 * 2 * (64 + 2) * 4
+    # up to 4 splits (G <= 8) are finished inside the workgroup: no workspace
+    assert L.pa_decode_workspace_bytes(pool, 8, 32, 4 * pages_one_split) == 0
+    n = L.pa_decode_workspace_bytes(pool, 8, 32, 4 * pages_one_split + 1)
+    assert n >= 8 * 32 * 5 * (64 + 2) * 4
+    # more than 8 query heads per KV head: 2 splits per workgroup
+    assert L.pa_decode_workspace_bytes(pool, 8, 128, 2 * pages_one_split) == 0
+    assert L.pa_decode_workspace_bytes(pool, 8, 128, 2 * pages_one_split + 1) >= 8 * 128 * 3 * 66 * 4
     assert L.pa_decode_workspace_bytes(None, 8, 32, 100) == 0
     assert L.pa_decode_workspace_bytes(pool, 0, 32, 100) == 0
+    assert L.pa_decode_workspace_bytes(pool, 8, 12, 100) == 0     # 12 heads over 8 KV heads
     L.pa_pool_destroy(pool)
 
 
@@ -160,65 +166,142 @@ def test_profile_and_status_strings():
 
 # ---- launch plan (pure host code)
 
-def expected_plan(ctx, stride, split_pages=64, kv_heads=8, wgs_per_cu=4):
-    """Every (sequence, split) that exists, sorted by page count descending, then
-    sequence, then split; an empty context keeps one zero-page item. When the
-    grid fits the device at once (items x kv heads <= 256 CUs x workgroups per
-    CU), every other tier of 32 items is reversed."""
-    items = []
+def expected_plan(ctx, stride, group=4, d=64, kv_heads=8, rounds_min=1):
+    """The decode plan, restated: units are splits (2048 tokens at d = 64,
+    1024 at d = 128); a sequence with at most ucap splits (4, or 2 when
+    G > 8) is one group, a longer one a group per split, an empty context one
+    zero-pair unit. Groups by pairs (largest first, stable) go to the bin with
+    the fewest pairs (then the lowest index) that has room for their units,
+    among rounds x (256 / kv_heads) bins; a group no bin has room for opens a
+    new bin. Bins with units, by pairs (largest first, stable), become items of
+    8 words: units b | s << 20 (-1 for none), then the rotations (pairs before
+    the unit in its item, mod W, 4 bits per unit), then three zeros."""
+    sp, w = (128, 16) if d == 64 else (64, 8)
+    ucap = 4 if group <= 8 else 2
+    groups = []          # (pairs, [(b, s, unit pairs)])
     for b, n in enumerate(ctx):
         n = min(max(int(n), 0), stride * 16)
         pages = (n + 15) // 16
-        if pages == 0:
-            items.append((0, b, 0))
-            continue
-        for s in range((pages + split_pages - 1) // split_pages):
-            items.append((min(pages - s * split_pages, split_pages), b, s))
-    items.sort(key=lambda t: (-t[0], t[1], t[2]))
-    out = [b | (s << 20) for _, b, s in items]
-    if len(out) * kv_heads <= 256 * wgs_per_cu:
-        for t0 in range(32, len(out), 64):
-            out[t0:t0 + 32] = out[t0:t0 + 32][::-1]
+        ns = (pages + sp - 1) // sp
+        units = [(b, s, (min(pages - s * sp, sp) + 1) // 2) for s in range(ns)]
+        if ns == 0:
+            groups.append((0, [(b, 0, 0)]))
+        elif ns <= ucap:
+            groups.append((sum(u[2] for u in units), units))
+        else:
+            groups.extend((u[2], [u]) for u in units)
+    total_units = sum(len(g[1]) for g in groups)
+    slots = max(1, 256 // kv_heads)
+    rounds = max(rounds_min, -(-total_units // (ucap * slots)))
+    nbins = min(len(groups), rounds * slots)
+    bins = [[0, []] for _ in range(nbins)]
+    for pairs, units in sorted(groups, key=lambda g: -g[0]):
+        room = [i for i, bn in enumerate(bins) if ucap - len(bn[1]) >= len(units)]
+        if room:
+            i = min(room, key=lambda i: (bins[i][0], i))
+        else:
+            bins.append([0, []])
+            i = len(bins) - 1
+        bins[i][0] += pairs
+        bins[i][1].extend(units)
+    out = []
+    for pairs, units in sorted([bn for bn in bins if bn[1]], key=lambda bn: -bn[0]):
+        words = [-1] * 4 + [0] * 4
+        before = rot = 0
+        for k, (b, s, p) in enumerate(units):
+            words[k] = b | (s << 20)
+            rot |= (before % w) << (4 * k)
+            before += p
+        words[4] = rot
+        out.extend(words)
     return out
 
 
-def test_plan_order_and_clamping():
+def _plan_units(plan):
+    items = []
+    for i in range(0, len(plan), 8):
+        it = plan[i:i + 8]
+        items.append(([(x & 0xFFFFF, x >> 20) for x in it[:4] if x >= 0], it[4], it[5:]))
+    return items
+
+
+def test_plan_matches_its_statement_and_covers_every_unit():
     import numpy as np
     L = B.lib()
+    rng = np.random.default_rng(7)
+    for d, hkv, hq in [(64, 8, 32), (64, 8, 128), (128, 4, 28), (64, 2, 2)]:
+        h = make_pool(d=d, hkv=hkv)
+        pool = type("P", (), {"handle": h})()
+        g = hq // hkv
+        sp = 128 if d == 64 else 64
+        ucap = 4 if g <= 8 else 2
+        for stride in (1, 5, 64, 65, 129, 512, 700):
+            ctx = rng.integers(-3, stride * 16 + 40, 37).astype(np.int32)
+            ctx[:3] = [0, stride * 16, 1]
+            got = B.decode_plan(pool, ctx, hq, stride)
+            assert got.tolist() == expected_plan(ctx, stride, g, d, hkv)
+            cap = L.pa_decode_plan_capacity(h, len(ctx), stride)
+            assert cap == len(ctx) * -(-stride // sp) * 8 and len(got) <= cap
+            # every unit exactly once; short sequences whole and in split order
+            seen = {}
+            for units, rot, zeros in _plan_units(got.tolist()):
+                assert 1 <= len(units) <= ucap and list(zeros) == [0, 0, 0]
+                for k, (b, s) in enumerate(units):
+                    assert (b, s) not in seen
+                    seen[(b, s)] = (units, k)
+            for b, n in enumerate(ctx):
+                n = min(max(int(n), 0), stride * 16)
+                ns = -(-((n + 15) // 16) // sp)
+                want = [(b, s) for s in range(max(ns, 1))]
+                assert sorted(k for k in seen if k[0] == b) == want
+                if 1 < ns <= ucap:
+                    units, k = seen[(b, 0)]
+                    assert units[k:k + ns] == want
+        L.pa_pool_destroy(h)
+
+
+def test_plan_one_round_pairs_large_with_small():
+    """64 sequences of U[256, 2048] tokens over 8 KV heads (one split each):
+    32 items, one per CU of a device round, each the k-th largest sequence
+    with the k-th smallest."""
+    import numpy as np
     h = make_pool(d=64)
     pool = type("P", (), {"handle": h})()
-    rng = np.random.default_rng(7)
-    for stride in (1, 5, 64, 65, 512):
-        ctx = rng.integers(-3, stride * 16 + 40, 37).astype(np.int32)
-        ctx[:3] = [0, stride * 16, 1]
-        got = B.decode_plan(pool, ctx, stride)
-        assert got.tolist() == expected_plan(ctx, stride)
-        cap = L.pa_decode_plan_capacity(h, len(ctx), stride)
-        assert cap == len(ctx) * ((stride + 63) // 64)
-        assert len(got) <= cap
-    L.pa_pool_destroy(h)
+    ctx = np.random.default_rng(1003).integers(256, 2049, 64).astype(np.int32)
+    items = _plan_units(B.decode_plan(pool, ctx, 32, 128).tolist())
+    assert len(items) == 32
+    pages = -(-ctx // 16)
+    order = sorted(range(64), key=lambda b: -((pages[b] + 1) // 2))
+    pairs = sorted(((units[0][0], units[1][0]) for units, _, _ in items), key=lambda t: order.index(t[0]))
+    assert [p[0] for p in pairs] == order[:32]
+    loads = [((pages[a] + 1) // 2 + (pages[b] + 1) // 2) for a, b in pairs]
+    assert max(loads) - min(loads) <= 8
+    B.lib().pa_pool_destroy(h)
 
 
 def test_plan_validation():
     import numpy as np
     L = B.lib()
-    h = make_pool(d=128)
+    h = make_pool(d=128, hkv=4)
     n = ctypes.c_int32(-1)
     ctx = np.array([100, 5000, 0], dtype=np.int32)
-    buf = np.zeros(8, dtype=np.int32)
+    buf = np.zeros(64, dtype=np.int32)
     assert L.pa_decode_plan_capacity(None, 3, 10) == -1
     assert L.pa_decode_plan_capacity(h, 3, 0) == -1
     assert L.pa_decode_plan_capacity(h, (1 << 20) + 1, 10) == -1
     assert L.pa_decode_plan_capacity(h, 1, 64 * 2048 + 1) == -1
-    assert L.pa_decode_plan(h, ctx.ctypes.data, 3, 400, buf.ctypes.data, 8, None) == NULL
-    assert L.pa_decode_plan(h, None, 3, 400, buf.ctypes.data, 8, ctypes.byref(n)) == NULL
-    assert L.pa_decode_plan(h, ctx.ctypes.data, 3, 400, None, 8, ctypes.byref(n)) == NULL
-    # 5000 tokens = 313 pages = 5 splits; +1 for 100 tokens, +1 for the empty context
-    assert L.pa_decode_plan(h, ctx.ctypes.data, 3, 400, buf.ctypes.data, 6, ctypes.byref(n)) == INVALID
-    assert L.pa_decode_plan(h, ctx.ctypes.data, 3, 400, buf.ctypes.data, 8, ctypes.byref(n)) == OK
-    assert n.value == 7
-    assert buf[:7].tolist() == expected_plan(ctx, 400, kv_heads=8, wgs_per_cu=2)
-    assert L.pa_decode_plan(h, ctx.ctypes.data, 0, 400, None, 0, ctypes.byref(n)) == OK and n.value == 0
+    assert L.pa_decode_plan(h, ctx.ctypes.data, 3, 28, 400, buf.ctypes.data, 64, None) == NULL
+    assert L.pa_decode_plan(h, None, 3, 28, 400, buf.ctypes.data, 64, ctypes.byref(n)) == NULL
+    assert L.pa_decode_plan(h, ctx.ctypes.data, 3, 28, 400, None, 64, ctypes.byref(n)) == NULL
+    assert L.pa_decode_plan(h, ctx.ctypes.data, 3, 30, 400, buf.ctypes.data, 64, ctypes.byref(n)) == INVALID
+    assert L.pa_decode_plan(h, ctx.ctypes.data, 3, 4 * 17, 400, buf.ctypes.data, 64, ctypes.byref(n)) == UNSUPPORTED
+    # 5000 tokens = 5 splits of 1024 (more than 4: one group each), 100 tokens
+    # and the empty context one each: 7 units over 64 bins -> 7 items, 56 words
+    assert L.pa_decode_plan(h, ctx.ctypes.data, 3, 28, 400, buf.ctypes.data, 55, ctypes.byref(n)) == INVALID
+    assert L.pa_decode_plan(h, ctx.ctypes.data, 3, 28, 400, buf.ctypes.data, 56, ctypes.byref(n)) == OK
+    assert n.value == 56
+    assert buf[:56].tolist() == expected_plan(ctx, 400, 7, 128, 4)
+    assert L.pa_decode_plan(h, ctx.ctypes.data, 0, 28, 400, None, 0, ctypes.byref(n)) == OK and n.value == 0
     L.pa_pool_destroy(h)
 
 
@@ -227,16 +310,26 @@ def test_planned_decode_validation():
     h = make_pool(d=64)
     ws = 1 << 24
 
-    def call(plan=P, items=4, num_seqs=2, stride=70, ws_ptr=P, ws_bytes=ws):
+    def call(plan=P, words=8, num_seqs=2, stride=600, ws_ptr=P, ws_bytes=ws):
         return L.pa_decode_planned(h, P, num_seqs, 32, P, stride, P, 0.125, P2, ws_ptr, ws_bytes, plan,
-                                   items, None)
+                                   words, None)
 
     assert call(plan=None) == NULL
     assert call(plan=P + 2) == ALIGN
-    assert call(items=-1) == INVALID
-    assert call(items=5) == INVALID          # 2 sequences x 2 splits at most
-    assert call(ws_ptr=None, ws_bytes=0) == WORKSPACE
-    assert call(num_seqs=0, plan=None, items=0) == OK
+    assert call(words=-8) == INVALID
+    assert call(words=12) == INVALID         # not whole items of 8 words
+    assert call(words=2 * 5 * 8 + 8) == INVALID   # 2 sequences x 5 splits at most
+    assert call(ws_ptr=None, ws_bytes=0) == WORKSPACE   # 600 pages: 5 splits, more than 4
+    assert call(num_seqs=0, plan=None, words=0) == OK
+
+    def host(plan=P, words=8, num_seqs=300, stride=600):
+        return L.pa_decode_planned_host(h, P, num_seqs, 32, P, stride, P, 0.125, P2, P, ws, plan, words, None)
+
+    assert host(plan=None) == NULL
+    assert host(words=12) == INVALID
+    assert host(words=2048 + 8) == INVALID    # more than the kernel arguments carry
+    assert host(words=-8) == INVALID
+    assert host(num_seqs=0, plan=None, words=0) == OK
     L.pa_pool_destroy(h)
 
 
@@ -268,23 +361,6 @@ def test_prefill_and_write_validation():
     assert L.pa_kv_write(h, P, P, 1, 4, 4, P, P, 0, P, None) == INVALID
     assert L.pa_kv_write(h, None, None, 0, 4, 4, None, None, 2, None, None) == OK
     L.pa_pool_destroy(h)
-
-
-def test_plan_tiers_reversed_only_when_the_grid_fits_at_once():
-    import numpy as np
-    h = make_pool(d=64)                       # 8 KV heads, 4 decode workgroups per CU: 1024 resident
-    pool = type("P", (), {"handle": h})()
-    rng = np.random.default_rng(3)
-    small = rng.integers(1, 1025, 100).astype(np.int32)     # 100 items x 8 = 800: one round
-    got = B.decode_plan(pool, small, 64)
-    assert got.tolist() == expected_plan(small, 64)
-    plain = sorted(range(100), key=lambda b: (-(-(-int(small[b]) // 16)), b))
-    assert got[:32].tolist() == plain[:32] and got[32:64].tolist() == plain[32:64][::-1]
-    assert got[64:96].tolist() == plain[64:96] and got[96:].tolist() == plain[96:][::-1]
-    large = rng.integers(1, 1025, 200).astype(np.int32)     # 200 x 8 = 1600: several rounds
-    got = B.decode_plan(pool, large, 64)
-    assert got.tolist() == sorted(range(200), key=lambda b: (-(-(-int(large[b]) // 16)), b))
-    B.lib().pa_pool_destroy(h)
 
 
 def expected_prefill_plan(ctx, chunks, hq, hkv, stride, max_chunk, d=64):

@@ -1,8 +1,8 @@
 """The library's host code (csrc/pakv.hip: argument checks, sizing, the
 decode launch plan) with AddressSanitizer and UBSan on its host side, driven
-from C by tests/c_client/abi_fuzz.c: random plans into buffers of exactly
-the stated capacity (every (sequence, split) once, largest first), the
-sizing calls, every status text, and the argument checks of every entry
+from C by tests/c_client/abi_fuzz.c: random plans (every (sequence, split)
+once, short sequences whole in one item, rotations and item order as stated;
+a buffer one word short refused untouched), the sizing calls, every status text, and the argument checks of every entry
 point that queues work, with arguments they must refuse (so no kernel is
 ever queued). CPU only."""
 

@@ -24,7 +24,7 @@ def test_graph_replay_matches_eager(d, hq, hkv):
     up = Uploaded(w, dev)
     eager = up.step(fused=False, planned=True).clone()
     k_eager, v_eager = up.k_pool.clone(), up.v_pool.clone()
-    plan = torch.from_numpy(B.decode_plan(up.pool, w.ctx_lens, w.stride)).to(dev)
+    plan = torch.from_numpy(B.decode_plan(up.pool, w.ctx_lens, w.num_q_heads, w.stride)).to(dev)
     stream = torch.cuda.Stream()
 
     def layers(s):

@@ -52,7 +52,7 @@ def test_c5_full_launch_all_outputs():
     log(f"c5: B=64 Hq=28 Hkv=4 d=128 pages={w.num_pages} max_ctx={w.ctx_lens.max()} "
         f"entry=pa_decode_planned, oracle on {host_workers()} host workers")
     up = Uploaded(w, dev)
-    out = up.step(planned=True).cpu().numpy()
+    out = up.step(planned="host").cpu().numpy()
     torch.cuda.synchronize()
     plain = up.step().cpu().numpy()
     assert np.array_equal(plain, out), "c5: planned != plain"
@@ -76,9 +76,12 @@ def test_c4_full_step_all_sequences():
     log(f"c4: L=16 B=256 pages={w.num_pages} max_ctx={w.ctx_lens.max()} "
         f"entry=pa_kv_append+pa_decode_planned, oracle on {host_workers()} host workers")
     up = Uploaded(w, dev)
-    out = up.step(fused=False, planned=True).cpu().numpy()   # the step the benchmark times
+    out = up.step(fused=False, planned="host").cpu().numpy()   # the step the benchmark times
     torch.cuda.synchronize()
-    # the plan changes only the launch order: pa_decode gives the same bits
+    # the plan changes only the launch order: pa_decode and the device plan
+    # give the same bits
+    dev_planned = up.step(fused=False, planned="device").cpu().numpy()
+    assert np.array_equal(dev_planned, out), "c4: device plan != host plan"
     for layer in (0, 15):
         plain = B.decode(up.pool, up.q[layer], up.bt[layer], up.ctx, float(w.scale), workspace=up.workspace)
         assert np.array_equal(plain.cpu().numpy(), out[layer]), f"c4 layer {layer}: planned != plain"
@@ -115,17 +118,22 @@ EDGE_CASES = [
     # (label, ctx_lens, Hq, Hkv, d)
     ("empty_and_one", [0, 1, 0, 2, 3], 32, 8, 64),
     ("page_boundaries", [15, 16, 17, 31, 32, 33, 47, 48, 49], 32, 8, 64),
-    ("split_boundaries", [511, 512, 513, 1023, 1024, 1025, 1535], 32, 8, 64),
-    ("long_d64", [8192, 4099, 6000], 32, 8, 64),
-    ("mha_group1", [100, 300, 7], 8, 8, 64),
-    ("group2_one_kv", [77, 600], 2, 1, 64),
-    ("group16", [250, 513, 33], 32, 2, 64),
+    # 2048-token splits at d = 64: up to 4 finished inside the workgroup, 5+ by the merge kernel
+    ("split_boundaries", [2047, 2048, 2049, 4095, 4096, 4097, 8191, 8192, 8193], 32, 8, 64),
+    ("split_boundaries_d128", [1023, 1024, 1025, 2047, 2048, 4096, 4097], 28, 4, 128),
+    ("long_d64", [8192, 4099, 6000, 12000], 32, 8, 64),
+    ("mha_group1", [100, 300, 7, 9000], 8, 8, 64),
+    ("group2_one_kv", [77, 600, 5000], 2, 1, 64),
+    # G = 16: a workgroup finishes at most 2 splits
+    ("group16", [250, 513, 33, 4096, 4200, 6000], 32, 2, 64),
     ("group7_d128", [1, 17, 512, 513, 2000, 4097], 28, 4, 128),
-    ("group8_d128", [300, 1100], 8, 1, 128),
-    ("group16_d128", [65, 1500], 32, 2, 128),
+    ("group8_d128", [300, 1100, 4500], 8, 1, 128),
+    ("group16_d128", [65, 1500, 2048, 3000], 32, 2, 128),
     ("long_d128", [16384, 12345], 28, 4, 128),
     ("beyond_64_splits_d64", [70000, 3, 65537], 32, 8, 64),
+    ("beyond_64_splits_d128", [70000, 3, 66000], 28, 4, 128),
     ("ragged_many", list(np.random.default_rng(4).integers(0, 700, 37)), 32, 8, 64),
+    ("ragged_many_long", list(np.random.default_rng(5).integers(0, 9000, 45)), 32, 8, 64),
 ]
 
 
@@ -141,6 +149,8 @@ def test_edge_cases(label, ctx, hq, hkv, d):
     a, r = check_parity(out, ref, label)
     planned = up.step(fused=False, planned=True).cpu().numpy()
     assert np.array_equal(planned, out), f"{label}: pa_decode_planned differs from pa_decode"
+    planned = up.step(fused=False, planned="host").cpu().numpy()
+    assert np.array_equal(planned, out), f"{label}: pa_decode_planned_host differs from pa_decode"
     for b, n in enumerate(w.ctx_lens):
         if n == 0:
             assert np.array_equal(out[0, b], np.zeros_like(out[0, b])), "ctx 0 must give zeros"
@@ -150,7 +160,7 @@ def test_edge_cases(label, ctx, hq, hkv, d):
 def test_full_block_table_context():
     """Contexts that fill every entry of the block table (stride * 16 tokens)."""
     dev = device()
-    for d, hq, hkv, stride in [(64, 32, 8, 40), (128, 28, 4, 70)]:
+    for d, hq, hkv, stride in [(64, 32, 8, 40), (128, 28, 4, 70), (64, 32, 8, 600), (128, 28, 4, 300)]:
         ctx = [stride * 16, stride * 16 - 5, 1]
         w = W.custom(seed=31 + d, ctx_lens=ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
                      stride=stride)

@@ -37,22 +37,36 @@ def test_determinism_ten_runs():
 
 
 def test_batch_invariance_bitwise():
+    """A sequence's output bits do not depend on the batch around it, with or
+    without a launch plan (which packs different sequences into one
+    workgroup depending on the batch): one-split, whole-in-workgroup
+    (2..4 splits) and merge-kernel (5+ splits) sequences."""
     import torch
     dev = device()
-    ctx = [700, 5, 1500, 33, 0, 260]
+    ctx = [700, 5, 1500, 33, 0, 260, 5000, 9000, 2049]
     w = W.custom(seed=8, ctx_lens=ctx)
     log(f"batch invariance ctx={ctx}")
     up = Uploaded(w, dev)
     full = up.step()[0].clone()
-    for b in range(len(ctx)):
-        out = B.decode(up.pool, up.q[0][b:b + 1].contiguous(), up.bt[0][b:b + 1].contiguous(),
-                       up.ctx[b:b + 1].contiguous(), float(w.scale))
-        assert bool((out[0] == full[b]).all()), f"sequence {b} differs alone vs in the batch"
-    # and inside a bigger, different batch
-    idx = torch.tensor([3, 2, 2, 0], device=dev)
-    out = B.decode(up.pool, up.q[0][idx].contiguous(), up.bt[0][idx].contiguous(),
-                   up.ctx[idx].contiguous(), float(w.scale))
-    assert bool((out == full[idx]).all())
+    planned = up.step(fused=False, planned=True)[0].clone()
+    assert bool((planned == full).all()), "planned batch differs from the plain batch"
+
+    def run(idx, plan):
+        ix = torch.tensor(idx, device=dev)
+        q, bt, c = up.q[0][ix].contiguous(), up.bt[0][ix].contiguous(), up.ctx[ix].contiguous()
+        if not plan:
+            return B.decode(up.pool, q, bt, c, float(w.scale))
+        p = torch.from_numpy(B.decode_plan(up.pool, w.ctx_lens[idx], w.num_q_heads, w.stride)).to(dev)
+        return B.decode_planned(up.pool, q, bt, c, float(w.scale), p)
+
+    for plan in (False, True):
+        for b in range(len(ctx)):
+            out = run([b], plan)
+            assert bool((out[0] == full[b]).all()), f"sequence {b} differs alone vs in the batch (plan={plan})"
+        # and inside bigger, different batches
+        for idx in ([3, 2, 2, 0], [7, 1, 6, 6, 3, 8, 0, 5], [8, 7, 6, 5, 4, 3, 2, 1, 0, 7, 2]):
+            out = run(idx, plan)
+            assert bool((out == full[torch.tensor(idx, device=dev)]).all()), f"batch {idx} (plan={plan})"
 
 
 def test_page_permutation_invariance_bitwise():
@@ -198,7 +212,7 @@ def test_out_of_range_inputs_stay_in_bounds():
 def test_error_paths_on_gpu():
     import torch
     dev = device()
-    w = W.custom(seed=14, ctx_lens=[2500, 700])         # more than one split: needs workspace
+    w = W.custom(seed=14, ctx_lens=[9000, 700])         # 5 splits of 2048: needs the workspace
     up = Uploaded(w, dev)
     log("error paths")
     small = torch.empty(16, dtype=torch.uint8, device=dev)
@@ -243,9 +257,12 @@ def test_binding_rejects_mismatched_shapes():
         args.update(bad)
         with pytest.raises(ValueError):
             B.decode(up.pool, args["q"], args["bt"], args["ctx"], 0.125, out=args["out"])
-        plan = torch.from_numpy(B.decode_plan(up.pool, w.ctx_lens, w.stride)).to(dev)
+        plan = torch.from_numpy(B.decode_plan(up.pool, w.ctx_lens, w.num_q_heads, w.stride)).to(dev)
         with pytest.raises(ValueError):
             B.decode_planned(up.pool, args["q"], args["bt"], args["ctx"], 0.125, plan, out=args["out"])
+        with pytest.raises(ValueError):
+            B.decode_planned_host(up.pool, args["q"], args["bt"], args["ctx"], 0.125, plan.cpu().numpy(),
+                                  out=args["out"])
     bad_rows = [
         dict(kn=kn[:2].contiguous()),
         dict(vn=torch.zeros((3, 8, 32), dtype=torch.int16, device=dev)),
@@ -298,10 +315,11 @@ def test_planned_decode_is_bitwise_plain_decode(case):
     up = Uploaded(w, dev)
     plain = up.step().clone()
     stride = w.block_tables.shape[-1]
-    plan_host = B.decode_plan(up.pool, w.ctx_lens, stride)
-    # items out of range are skipped on the device
+    plan_host = B.decode_plan(up.pool, w.ctx_lens, w.num_q_heads, stride)
+    # units out of range are skipped on the device: an item naming a sequence
+    # past the batch and a split past the grid
     s_max = -(-stride // (B.split_tokens(w.head_dim) // 16))
-    bogus = np.array([w.num_seqs + 5, (s_max << 20) | 0], dtype=np.int32)
+    bogus = np.array([w.num_seqs + 5, (s_max << 20) | 0, -1, -1, 0, 0, 0, 0], dtype=np.int32)
     for extra in (np.zeros(0, np.int32), bogus):
         p = np.concatenate([plan_host, extra])
         if p.size > B.lib().pa_decode_plan_capacity(up.pool.handle, w.num_seqs, stride):
@@ -312,6 +330,12 @@ def test_planned_decode_is_bitwise_plain_decode(case):
                          workspace=up.workspace)
         torch.cuda.synchronize()
         assert bool((out == plain[0]).all()), f"{case}: planned decode differs from pa_decode"
+        if p.size <= 2048:      # the same plan in the kernel's arguments
+            out2 = torch.full_like(plain[0], float("nan"))
+            B.decode_planned_host(up.pool, up.q[0], up.bt[0], up.ctx, float(w.scale), p, out=out2,
+                                  workspace=up.workspace)
+            torch.cuda.synchronize()
+            assert bool((out2 == plain[0]).all()), f"{case}: host-planned decode differs from pa_decode"
     if case == "custom":
         ref = oracle.decode_attention(up.q_host[0], w.pool_bits("k"), w.pool_bits("v"),
                                       w.block_tables[0], w.ctx_lens, w.scale)

@@ -68,7 +68,7 @@ class HostCase:
         q = self.q if q_bits is None else torch.from_numpy(q_bits.view(np.int16)).to(self.q.device)
         out = B.decode(self.pool, q, self.bt, self.ctx, float(scale)).cpu().numpy()
         # the planned launch must give the same bits
-        plan = torch.from_numpy(B.decode_plan(self.pool, self.w.ctx_lens, self.w.stride)).to(self.q.device)
+        plan = torch.from_numpy(B.decode_plan(self.pool, self.w.ctx_lens, self.w.num_q_heads, self.w.stride)).to(self.q.device)
         planned = B.decode_planned(self.pool, q, self.bt, self.ctx, float(scale), plan).cpu().numpy()
         assert np.array_equal(out, planned), "pa_decode_planned differs from pa_decode"
         return out
