@@ -10,16 +10,11 @@
 #include <cmath>
 #include <cstdint>
 #include <new>
+#include <queue>
 #include <vector>
 
 #include "pakv_kernels.h"
 #include "pakv_prefill.h"
-
-// Rounds of work items (one decode workgroup per CU) the launch plan aims
-// for when it packs units into items: more rounds, smaller items.
-#ifndef PAKV_PLAN_ROUNDS
-#define PAKV_PLAN_ROUNDS 1
-#endif
 
 struct pa_pool {
   void* k;
@@ -59,6 +54,12 @@ int prefill_wgs_per_cu(int d) {
 
 // decode workgroups one CU holds at once (waves per SIMD x 4 SIMDs / waves per workgroup)
 int decode_wgs_per_cu(int d) { return std::max(1, pakv::occupancy(d) * 4 / decode_waves(d)); }
+
+// Workgroups per KV head that the device holds at once: the bins of a plan.
+int64_t decode_slots(const pa_pool* pool) {
+  return std::max<int64_t>(1, static_cast<int64_t>(kDeviceCUs) * decode_wgs_per_cu(pool->head_dim) /
+                                  pool->num_kv_heads);
+}
 
 int64_t splits_for(int d, int32_t max_pages_per_seq) {
   const int64_t sp = split_pages(d);
@@ -132,17 +133,18 @@ struct LaunchTimer {
 
 template <int D, int NW>
 pa_status launch_decode_with(const pakv::DecodeArgs& args, const pakv::InlinePlan<NW>& ip, int64_t items,
-                             hipStream_t stream) {
+                             int64_t bins, hipStream_t stream) {
   (void)hipGetLastError();
   if (items == 0) return PA_OK;
   if (items > INT_MAX) return PA_ERR_INVALID;
   {
     LaunchTimer t(0, stream);
-    // x: KV head, (y, z): work item (y below 65536)
-    const unsigned gy = static_cast<unsigned>(std::min<int64_t>(items, 65535));
-    const unsigned gz = static_cast<unsigned>((items + 65534) / 65535);
+    // x: KV head, (y, z): bin (y below 65536)
+    const unsigned gy = static_cast<unsigned>(std::min<int64_t>(bins, 65535));
+    const unsigned gz = static_cast<unsigned>((bins + 65534) / 65535);
     pakv::DecodeArgs a = args;
     a.num_items = static_cast<int32_t>(items);
+    a.num_bins = static_cast<int32_t>(bins);
     hipLaunchKernelGGL((pakv::decode_kernel<D, NW>), dim3(static_cast<unsigned>(args.num_kv_heads), gy, gz),
                        dim3(64 * pakv::DecodeGeom<D>::W), 0, stream, a, ip);
   }
@@ -165,21 +167,21 @@ pa_status launch_decode_with(const pakv::DecodeArgs& args, const pakv::InlinePla
 // arguments (NULL: the device plan in args, or none)
 template <int D>
 pa_status launch_decode(const pakv::DecodeArgs& args, const int32_t* plan_host, int32_t plan_ints, int64_t items,
-                        hipStream_t stream) {
+                        int64_t bins, hipStream_t stream) {
   if (plan_host && plan_ints <= pakv::kInlineSmall) {
     pakv::InlinePlan<pakv::kInlineSmall> ip;
     std::copy(plan_host, plan_host + plan_ints, ip.w);
     std::fill(ip.w + plan_ints, ip.w + pakv::kInlineSmall, 0);
-    return launch_decode_with<D>(args, ip, items, stream);
+    return launch_decode_with<D>(args, ip, items, bins, stream);
   }
   if (plan_host) {
     pakv::InlinePlan<pakv::kInlineLarge> ip;
     std::copy(plan_host, plan_host + plan_ints, ip.w);
     std::fill(ip.w + plan_ints, ip.w + pakv::kInlineLarge, 0);
-    return launch_decode_with<D>(args, ip, items, stream);
+    return launch_decode_with<D>(args, ip, items, bins, stream);
   }
   pakv::InlinePlan<pakv::kItemInts> none{};
-  return launch_decode_with<D>(args, none, items, stream);
+  return launch_decode_with<D>(args, none, items, bins, stream);
 }
 
 }  // namespace
@@ -324,12 +326,16 @@ static pa_status decode_impl(const pa_pool* pool, const void* q, int32_t num_seq
   a.ucap = pakv::units_cap(group);
   a.scale_log2 = scale_log2_of(scale);
   a.plan = plan_host ? nullptr : plan;
-  // work items: the plan's, or per sequence its splits in groups of ucap
-  const int64_t items = (plan || plan_host) ? plan_ints / pakv::kItemInts
-                                            : static_cast<int64_t>(num_seqs) * ((s_max + a.ucap - 1) / a.ucap);
+  // work items: the plan's (the first min(slots, items) of them head the
+  // bins' chains), or per sequence its splits in groups of ucap, one item
+  // per workgroup
+  const bool planned = plan || plan_host;
+  const int64_t items = planned ? plan_ints / pakv::kItemInts
+                                : static_cast<int64_t>(num_seqs) * ((s_max + a.ucap - 1) / a.ucap);
+  const int64_t bins = planned ? std::min(items, decode_slots(pool)) : items;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (d == 64) return launch_decode<64>(a, plan_host, plan_ints, items, s);
-  return launch_decode<128>(a, plan_host, plan_ints, items, s);
+  if (d == 64) return launch_decode<64>(a, plan_host, plan_ints, items, bins, s);
+  return launch_decode<128>(a, plan_host, plan_ints, items, bins, s);
 }
 
 pa_status pa_decode(const pa_pool* pool, const void* q, int32_t num_seqs, int32_t num_q_heads,
@@ -373,18 +379,24 @@ pa_status pa_decode_plan(const pa_pool* pool, const int32_t* context_lens_host, 
 }
 
 // The plan packs units (splits of one sequence) into work items of at most
-// ucap units, one workgroup per item and KV head:
+// ucap units, and items into bins, one workgroup per bin and KV head that
+// runs its bin's items in turn:
 //  - a sequence of at most ucap splits is one indivisible group (its splits
 //    are merged inside the workgroup); a longer one gives one group per
 //    split (merged by the merge kernel);
-//  - groups go, largest first, to the item with the fewest pairs that has
-//    room for them, over as many items as one round of the device holds
-//    (256 CUs, one workgroup each, Hkv workgroups per item) times the rounds
-//    the unit count needs; an item runs out of room only by its unit count;
-//  - items are listed by pairs, largest first, so that a grid of several
-//    rounds ends on its smallest items.
+//  - a group costs its pairs plus kUnitCost per unit (an item's fixed work,
+//    the start of its stream and its merge, shared by its units); groups go,
+//    costliest first, each to the bin of least cost so far, over as many
+//    bins as the device holds workgroups at once (or one per group, if there
+//    are fewer groups), so that the bins end together;
+//  - in each bin, its groups in that order go to the first of its items with
+//    room for them (a new item when none has);
+//  - item b (b < bins) is bin b's first item; each item names the bin's next
+//    one, listed after all the first items.
 // A unit's rotation is the number of pairs before it in its item, mod W:
 // the workgroup's waves then deal all of the item's pairs round-robin.
+constexpr int64_t kUnitCost = 5;
+
 static pa_status decode_plan_impl(const pa_pool* pool, const int32_t* context_lens_host, int32_t num_seqs,
                                   int group, int32_t max_pages_per_seq, int32_t* plan, int64_t capacity,
                                   int32_t* num_ints) {
@@ -394,7 +406,7 @@ static pa_status decode_plan_impl(const pa_pool* pool, const int32_t* context_le
   const int ucap = pakv::units_cap(group);
   const int64_t max_tok = static_cast<int64_t>(max_pages_per_seq) * pakv::kPage;
   struct Group {
-    int64_t pairs;
+    int64_t pairs, cost;
     int32_t b, s0, units;
   };
   auto split_pairs = [&](int64_t pages, int64_t s) {
@@ -402,92 +414,84 @@ static pa_status decode_plan_impl(const pa_pool* pool, const int32_t* context_le
   };
   std::vector<Group> groups;
   groups.reserve(static_cast<size_t>(num_seqs));
-  int64_t total_units = 0;
   for (int32_t b = 0; b < num_seqs; ++b) {
     const int64_t n = std::min<int64_t>(std::max(context_lens_host[b], 0), max_tok);
     const int64_t pages = (n + pakv::kPage - 1) / pakv::kPage;
     const int64_t ns = (pages + sp - 1) / sp;
     if (ns <= 1) {   // an empty context keeps one unit: it writes the zero output
-      groups.push_back({ns ? split_pairs(pages, 0) : 0, b, 0, 1});
-      total_units += 1;
+      const int64_t p = ns ? split_pairs(pages, 0) : 0;
+      groups.push_back({p, p + kUnitCost, b, 0, 1});
     } else if (ns <= ucap) {
       int64_t p = 0;
       for (int64_t s = 0; s < ns; ++s) p += split_pairs(pages, s);
-      groups.push_back({p, b, 0, static_cast<int32_t>(ns)});
-      total_units += ns;
+      groups.push_back({p, p + kUnitCost * ns, b, 0, static_cast<int32_t>(ns)});
     } else {
-      for (int64_t s = 0; s < ns; ++s) groups.push_back({split_pairs(pages, s), b, static_cast<int32_t>(s), 1});
-      total_units += ns;
+      for (int64_t s = 0; s < ns; ++s) {
+        const int64_t p = split_pairs(pages, s);
+        groups.push_back({p, p + kUnitCost, b, static_cast<int32_t>(s), 1});
+      }
     }
   }
-  std::stable_sort(groups.begin(), groups.end(), [](const Group& x, const Group& y) { return x.pairs > y.pairs; });
-  const int64_t slots = std::max<int64_t>(1, kDeviceCUs * decode_wgs_per_cu(d) / pool->num_kv_heads);
-  const int64_t rounds = std::max<int64_t>(PAKV_PLAN_ROUNDS, (total_units + ucap * slots - 1) / (ucap * slots));
-  const int64_t nbins = std::min<int64_t>(static_cast<int64_t>(groups.size()), rounds * slots);
-  struct Bin {
-    int64_t pairs = 0;
+  std::stable_sort(groups.begin(), groups.end(), [](const Group& x, const Group& y) { return x.cost > y.cost; });
+  const int64_t nb = std::min<int64_t>(static_cast<int64_t>(groups.size()), decode_slots(pool));
+  // groups to bins: least cost first, ties to the lower bin
+  std::vector<std::vector<int32_t>> bin_groups(static_cast<size_t>(nb));
+  typedef std::pair<int64_t, int64_t> Key;
+  std::priority_queue<Key, std::vector<Key>, std::greater<Key>> heap;
+  for (int64_t i = 0; i < nb; ++i) heap.push({0, i});
+  for (size_t gi = 0; gi < groups.size(); ++gi) {
+    const Key k = heap.top();
+    heap.pop();
+    bin_groups[static_cast<size_t>(k.second)].push_back(static_cast<int32_t>(gi));
+    heap.push({k.first + groups[gi].cost, k.second});
+  }
+  // each bin's groups to its items, first fit
+  struct Item {
     int units = 0;
     std::vector<int32_t> members;   // group indices, in the order placed
   };
-  std::vector<Bin> bins(static_cast<size_t>(nbins));
-  // bins by free unit count, each a min-heap on (pairs, index)
-  typedef std::pair<int64_t, int64_t> Key;
-  std::vector<std::vector<Key>> heaps(static_cast<size_t>(ucap) + 1);
-  auto greater = [](const Key& x, const Key& y) { return x > y; };
-  for (int64_t i = 0; i < nbins; ++i) heaps[ucap].push_back({0, i});
-  for (size_t gi = 0; gi < groups.size(); ++gi) {
-    const Group& g = groups[gi];
-    int best_f = -1;
-    for (int f = g.units; f <= ucap; ++f)
-      if (!heaps[f].empty() && (best_f < 0 || heaps[f].front() < heaps[best_f].front())) best_f = f;
-    int64_t bi;
-    if (best_f < 0) {
-      bi = static_cast<int64_t>(bins.size());
-      bins.emplace_back();
-    } else {
-      std::pop_heap(heaps[best_f].begin(), heaps[best_f].end(), greater);
-      bi = heaps[best_f].back().second;
-      heaps[best_f].pop_back();
-    }
-    Bin& bin = bins[static_cast<size_t>(bi)];
-    bin.pairs += g.pairs;
-    bin.units += g.units;
-    bin.members.push_back(static_cast<int32_t>(gi));
-    const int f = ucap - bin.units;
-    if (f > 0) {
-      heaps[f].push_back({bin.pairs, bi});
-      std::push_heap(heaps[f].begin(), heaps[f].end(), greater);
-    }
-  }
-  std::vector<int64_t> order;
-  order.reserve(bins.size());
-  for (size_t i = 0; i < bins.size(); ++i)
-    if (!bins[i].members.empty()) order.push_back(static_cast<int64_t>(i));
-  std::stable_sort(order.begin(), order.end(),
-                   [&](int64_t x, int64_t y) { return bins[static_cast<size_t>(x)].pairs > bins[static_cast<size_t>(y)].pairs; });
-  const int64_t ints = static_cast<int64_t>(order.size()) * pakv::kItemInts;
-  if (ints > capacity) return PA_ERR_INVALID;
-  int64_t w = 0;
-  for (int64_t bi : order) {
-    const Bin& bin = bins[static_cast<size_t>(bi)];
-    int32_t* it = plan + w;
-    for (int k = 0; k < pakv::kItemInts; ++k) it[k] = k < pakv::kItemUnits ? -1 : 0;
-    int u = 0;
-    int64_t before = 0;
-    uint32_t rot = 0;
-    for (int32_t gi : bin.members) {
+  std::vector<std::vector<Item>> bin_items(static_cast<size_t>(nb));
+  int64_t total = 0;
+  for (int64_t b = 0; b < nb; ++b) {
+    std::vector<Item>& items = bin_items[static_cast<size_t>(b)];
+    for (int32_t gi : bin_groups[static_cast<size_t>(b)]) {
       const Group& g = groups[static_cast<size_t>(gi)];
-      const int64_t n = std::min<int64_t>(std::max(context_lens_host[g.b], 0), max_tok);
-      const int64_t pages = (n + pakv::kPage - 1) / pakv::kPage;
-      for (int32_t k = 0; k < g.units; ++k, ++u) {
-        const int64_t s = g.s0 + k;
-        it[u] = static_cast<int32_t>(static_cast<uint32_t>(g.b) | (static_cast<uint32_t>(s) << 20));
-        rot |= static_cast<uint32_t>(before % W) << (4 * u);
-        before += pages > 0 ? split_pairs(pages, s) : 0;
-      }
+      size_t k = 0;
+      while (k < items.size() && items[k].units + g.units > ucap) ++k;
+      if (k == items.size()) items.emplace_back();
+      items[k].units += g.units;
+      items[k].members.push_back(gi);
     }
-    it[pakv::kItemUnits] = static_cast<int32_t>(rot);
-    w += pakv::kItemInts;
+    total += static_cast<int64_t>(items.size());
+  }
+  const int64_t ints = total * pakv::kItemInts;
+  if (ints > capacity) return PA_ERR_INVALID;
+  int64_t extra = nb;   // index of the next item listed after the first ones
+  for (int64_t b = 0; b < nb; ++b) {
+    const std::vector<Item>& items = bin_items[static_cast<size_t>(b)];
+    int64_t idx = b;
+    for (size_t k = 0; k < items.size(); ++k) {
+      const int64_t nxt = k + 1 < items.size() ? extra++ : 0;
+      int32_t* it = plan + idx * pakv::kItemInts;
+      for (int j = 0; j < pakv::kItemInts; ++j) it[j] = j < pakv::kItemUnits ? -1 : 0;
+      int u = 0;
+      int64_t before = 0;
+      uint32_t rot = 0;
+      for (int32_t gi : items[k].members) {
+        const Group& g = groups[static_cast<size_t>(gi)];
+        const int64_t n = std::min<int64_t>(std::max(context_lens_host[g.b], 0), max_tok);
+        const int64_t pages = (n + pakv::kPage - 1) / pakv::kPage;
+        for (int32_t j = 0; j < g.units; ++j, ++u) {
+          const int64_t s = g.s0 + j;
+          it[u] = static_cast<int32_t>(static_cast<uint32_t>(g.b) | (static_cast<uint32_t>(s) << 20));
+          rot |= static_cast<uint32_t>(before % W) << (4 * u);
+          before += pages > 0 ? split_pairs(pages, s) : 0;
+        }
+      }
+      it[pakv::kItemUnits] = static_cast<int32_t>(rot);
+      it[pakv::kItemUnits + 1] = static_cast<int32_t>(nxt);
+      idx = nxt;
+    }
   }
   *num_ints = static_cast<int32_t>(ints);
   return PA_OK;

@@ -88,7 +88,7 @@ template <> struct DecodeGeom<128> {
 };
 
 constexpr int kItemUnits = 4;   // units a work item can name
-constexpr int kItemInts = 8;    // int32 words per plan item: 4 units, the rotations, 3 unused
+constexpr int kItemInts = 8;    // int32 words per plan item: 4 units, the rotations, the next item, 2 unused
 constexpr int kMaxPairsPerUnit = 4;
 // Units a workgroup can finish together: the LDS holds the partials of
 // (units x G) <= 32 query-head rows per wave.
@@ -111,12 +111,16 @@ struct DecodeArgs {
   int32_t stride;     // max_pages_per_seq
   int32_t s_max;      // splits per sequence the grid covers
   int32_t ucap;       // units_cap(group)
-  int32_t num_items;  // work items in the grid
+  int32_t num_items;  // work items the plan lists (or the grid covers, without one)
+  int32_t num_bins;   // workgroups per KV head: the grid's (y, z) extent
   float scale_log2;   // scale * log2(e)
-  // optional launch plan: workgroup (item, KV head) runs the units of
-  // plan[item * kItemInts + 0..3] (b | s << 20, or -1 for none) with the
-  // rotations packed 4 bits per unit in plan[item * kItemInts + 4]; NULL =
-  // per sequence, its splits in consecutive groups of ucap
+  // optional launch plan: workgroup (bin, KV head) runs item bin, then the
+  // chain of items each item names as its next. Item i runs the units of
+  // plan[i * kItemInts + 0..3] (b | s << 20, or -1 for none) with the
+  // rotations packed 4 bits per unit in plan[i * kItemInts + 4]; its
+  // successor is plan[i * kItemInts + 5] (the chain ends at an index that is
+  // not above i, or not in [num_bins, num_items)). NULL = one item per
+  // workgroup: per sequence, its splits in consecutive groups of ucap.
   const int32_t* plan;
 };
 
@@ -448,34 +452,24 @@ __device__ __forceinline__ void lse_merge(int nsplit, int lane, ML ml, ACC acc, 
 // Waves per SIMD the register budget must allow (512 registers per lane).
 __host__ __device__ constexpr int occupancy(int d) { return d == 64 ? 4 : 2; }
 
+// One work item of KV head kvh: its units streamed by the workgroup's waves,
+// their partials merged. Returns the index of the item the plan chains after
+// it (-1 without a plan). Every wave of the workgroup takes the same path.
 template <int D, int NW>
-__global__ __launch_bounds__(64 * DecodeGeom<D>::W, occupancy(D)) void decode_kernel(DecodeArgs a,
-                                                                                   InlinePlan<NW> ip) {
-  static_assert(D == 64 || D == 128, "head_dim");
+__device__ __forceinline__ int decode_item(const DecodeArgs& a, const InlinePlan<NW>& ip, int kvh, int tid,
+                                           int item, float* smem) {
   constexpr int W = DecodeGeom<D>::W;
   constexpr int SP = DecodeGeom<D>::SPLIT_PAGES;
   constexpr int SPLIT_TOK = SP * kPage;
   constexpr int TILE = kPage * D;
-  static_assert(SP / 2 <= kMaxPairsPerUnit * W, "at most 4 pairs per logical wave");
-  static_assert((W & (W - 1)) == 0 && W <= 16, "W: a power of two, rotations in 4 bits");
   using L = DecodeLds<D>;
-  __shared__ __align__(16) float smem[L::TOTAL];
+  constexpr bool kInline = NW > kItemInts;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15;
   const int grp = lane >> 4;
   const int Hkv = a.num_kv_heads;
-  // grid: x = KV head, (y, z) = work item; linear workgroup order is KV head
-  // fastest, so with 8 KV heads each XCD takes one head of every item
-  const int kvh = blockIdx.x;
-  const int item = blockIdx.z * 65535 + blockIdx.y;
-  constexpr bool kInline = NW > kItemInts;
-  // only a grid past 65535 items has a ragged end; an inline plan holds at
-  // most 256 items, so its grid is exact
-  if constexpr (!kInline) {
-    if (item >= a.num_items) return;
-  }
   const int G = a.group;
   const int Hq = a.num_q_heads;
   const int ucap = a.ucap;
@@ -491,18 +485,20 @@ __global__ __launch_bounds__(64 * DecodeGeom<D>::W, occupancy(D)) void decode_ke
   const int stride = a.stride;
   int ub[kItemUnits], us[kItemUnits];
   int rot = 0;
+  int next = -1;
   if (kInline || a.plan) {
-    int it[kItemUnits + 1];
+    int it[kItemUnits + 2];
     if (kInline) {
 #pragma unroll
-      for (int k = 0; k <= kItemUnits; ++k) it[k] = ip.w[item * kItemInts + k];
+      for (int k = 0; k < kItemUnits + 2; ++k) it[k] = ip.w[item * kItemInts + k];
     } else {
 #pragma unroll
-      for (int k = 0; k <= kItemUnits; ++k) it[k] = a.plan[(size_t)item * kItemInts + k];
+      for (int k = 0; k < kItemUnits + 2; ++k) it[k] = a.plan[(size_t)item * kItemInts + k];
     }
     // every argument the next round of loads needs, in registers together
-    asm volatile("" ::"s"(it[0]), "s"(it[1]), "s"(it[2]), "s"(it[3]), "s"(it[4]), "s"(ctxp), "s"(btp), "s"(qp),
-                 "s"(num_seqs), "s"(s_max), "s"(stride));
+    asm volatile("" ::"s"(it[0]), "s"(it[1]), "s"(it[2]), "s"(it[3]), "s"(it[4]), "s"(it[5]), "s"(ctxp),
+                 "s"(btp), "s"(qp), "s"(num_seqs), "s"(s_max), "s"(stride));
+    next = it[kItemUnits + 1];
 #pragma unroll
     for (int u = 0; u < kItemUnits; ++u) {
       const int e = it[u];
@@ -523,7 +519,7 @@ __global__ __launch_bounds__(64 * DecodeGeom<D>::W, occupancy(D)) void decode_ke
       us[u] = s;
     }
   }
-  if (ub[0] < 0 && ub[1] < 0 && ub[2] < 0 && ub[3] < 0) return;
+  if (ub[0] < 0 && ub[1] < 0 && ub[2] < 0 && ub[3] < 0) return next;
 
   // the second round, issued together and unconditionally (absent units read
   // sequence 0, whose row always exists, and are masked after): the context
@@ -548,14 +544,14 @@ __global__ __launch_bounds__(64 * DecodeGeom<D>::W, occupancy(D)) void decode_ke
   const bool t_ok = lane < 32 && t_b >= 0 && t_lp < stride;
   int raw = btp[t_ok ? (size_t)t_b * stride + t_lp : 0];
   // query rows: 16-byte chunk t = (unit * 16 + head) * (D / 8) + c of the
-  // LDS copy, thread threadIdx.x + i * 64 * W for i < QCH
+  // LDS copy, thread tid + i * 64 * W for i < QCH
   constexpr int QCHUNKS = kItemUnits * 16 * (D / 8);
   constexpr int QCH = (QCHUNKS + 64 * W - 1) / (64 * W);
   u32x4 qv[QCH];
   bool qok[QCH];
 #pragma unroll
   for (int i = 0; i < QCH; ++i) {
-    const int t = threadIdx.x + i * 64 * W;
+    const int t = tid + i * 64 * W;
     const int u = (t / (16 * (D / 8))) & 3;
     const int h = (t / (D / 8)) & 15;
     const int ch = t % (D / 8);
@@ -616,7 +612,7 @@ __global__ __launch_bounds__(64 * DecodeGeom<D>::W, occupancy(D)) void decode_ke
     u32x4* sq = (u32x4*)(smem + L::Q);
 #pragma unroll
     for (int i = 0; i < QCH; ++i) {
-      const int t = threadIdx.x + i * 64 * W;
+      const int t = tid + i * 64 * W;
       const uint32_t m = -(uint32_t)qok[i];
       if (t < QCHUNKS) sq[t] = u32x4{qv[i][0] & m, qv[i][1] & m, qv[i][2] & m, qv[i][3] & m};
     }
@@ -659,7 +655,7 @@ __global__ __launch_bounds__(64 * DecodeGeom<D>::W, occupancy(D)) void decode_ke
 
   // merge each unit's W partials in logical-wave order
   const size_t head_kv = (size_t)kvh * G;
-  for (int e = threadIdx.x; e < kItemUnits * G * D; e += 64 * W) {
+  for (int e = tid; e < kItemUnits * G * D; e += 64 * W) {
     const int u = e / (G * D);
     const int rem = e - u * G * D;
     const int hh = rem / D;
@@ -702,7 +698,7 @@ __global__ __launch_bounds__(64 * DecodeGeom<D>::W, occupancy(D)) void decode_ke
       }
     }
   }
-  if (!any_whole) return;
+  if (!any_whole) return next;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -716,6 +712,46 @@ __global__ __launch_bounds__(64 * DecodeGeom<D>::W, occupancy(D)) void decode_ke
       auto acc = [&](int s, int e) { return smem[L::ACC + (size_t)(((u0 + s) * W) * G + hh) * L::ROW + e]; };
       lse_merge<D>(nsplit[u0], lane, ml, acc, a.out + ((size_t)ub[u0] * Hq + head_kv + hh) * D);
     }
+  }
+  return next;
+}
+
+// One workgroup per (KV head, bin): the bin's items in turn. Consecutive
+// items need no barrier between them: an item writes the query rows (read
+// only while streaming, which ended at the previous item's merge barrier)
+// before its first barrier, and the partials only after it, when every wave
+// has finished the previous item's merge.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * DecodeGeom<D>::W, occupancy(D)) void decode_kernel(DecodeArgs a,
+                                                                                   InlinePlan<NW> ip) {
+  static_assert(D == 64 || D == 128, "head_dim");
+  constexpr int W = DecodeGeom<D>::W;
+  constexpr int SP = DecodeGeom<D>::SPLIT_PAGES;
+  static_assert(SP / 2 <= kMaxPairsPerUnit * W, "at most 4 pairs per logical wave");
+  static_assert((W & (W - 1)) == 0 && W <= 16, "W: a power of two, rotations in 4 bits");
+  __shared__ __align__(16) float smem[DecodeLds<D>::TOTAL];
+  // grid: x = KV head, (y, z) = bin; linear workgroup order is KV head
+  // fastest, so with 8 KV heads each XCD takes one head of every bin
+  const int kvh = blockIdx.x;
+  const int bin = blockIdx.z * 65535 + blockIdx.y;
+  constexpr bool kInline = NW > kItemInts;
+  // only a grid past 65535 bins has a ragged end; an inline plan holds at
+  // most 256 items, so its grid is exact
+  if constexpr (!kInline) {
+    if (bin >= a.num_bins) return;
+  }
+  int item = bin;
+  for (;;) {
+    // each item derives its per-lane values afresh (opaque copies of the
+    // thread and KV head indices): none is held in registers across items
+    int h = kvh;
+    int tid = threadIdx.x;
+    asm volatile("" : "+s"(h), "+v"(tid));
+    const int next = decode_item<D, NW>(a, ip, h, tid, item, smem);
+    // a chain only moves forward, past the bins' first items and inside the
+    // plan: it ends after at most num_items items whatever the plan holds
+    if (next <= item || next < a.num_bins || next >= a.num_items) break;
+    item = next;
   }
 }
 

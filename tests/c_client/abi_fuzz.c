@@ -7,9 +7,11 @@
  *     existing (sequence, split) exactly once (an empty context once, as
  *     split 0); a sequence with 2 .. ucap splits whole, in split order, in one
  *     item; each unit's rotation the pairs before it in its item mod the
- *     workgroup's waves; items by pairs, largest first; and the same call
- *     into a buffer one word short of the plan refused, nothing written past
- *     it;
+ *     workgroup's waves; the bins' chains (item b < bins first, each item
+ *     naming the next) reach every item once, moving forward past the first
+ *     items; bin costs (pairs + 5 per unit) within one group's cost of each
+ *     other; and the same call into a buffer one word short of the plan
+ *     refused, nothing written past it;
  *   - pa_prefill_plan on random cache and chunk lengths (negative and past
  *     the bounds included): every row block that holds rows appears once
  *     and no other, costs never increase along the plan outside the
@@ -97,11 +99,14 @@ static void plan_round(long round) {
   }
   char* seen = (char*)calloc((size_t)(num_seqs ? num_seqs : 1) * 2048, 1);
   if (!seen) fail("oom", round);
-  int64_t prev_pairs = INT64_MAX;
+  const int32_t nitems = words / 8;
+  int64_t* item_cost = (int64_t*)calloc((size_t)(nitems ? nitems : 1), sizeof(int64_t));
+  if (!item_cost) fail("oom", round);
+  int64_t max_group = 0;
   int64_t placed = 0;
   for (int32_t i = 0; i < words; i += 8) {
     const int32_t* it = plan + i;
-    if (it[5] != 0 || it[6] != 0 || it[7] != 0) fail("unused words", round);
+    if (it[6] != 0 || it[7] != 0) fail("unused words", round);
     int nu = 0;
     int64_t before = 0, pairs_item = 0;
     for (int u = 0; u < 4; ++u) {
@@ -124,6 +129,12 @@ static void plan_round(long round) {
       before += (pg + 1) / 2;
       pairs_item += (pg + 1) / 2;
       if (s == 0 && ns >= 2 && ns <= ucap) {   /* a short sequence: whole, in order, from here */
+        int64_t gp = 0;
+        for (int64_t v = 0; v < ns; ++v) {
+          const int64_t pv = pages - v * sp < sp ? pages - v * sp : sp;
+          gp += (pv + 1) / 2;
+        }
+        if (gp + 5 * ns > max_group) max_group = gp + 5 * ns;
         if (u + ns > 4) fail("short sequence cut", round);
         for (int v = 1; v < ns; ++v)
           if (it[u + v] != (int32_t)((uint32_t)b | ((uint32_t)v << 20))) fail("short sequence cut", round);
@@ -133,10 +144,44 @@ static void plan_round(long round) {
     }
     if (nu == 0 || nu > ucap) fail("units per item", round);
     if ((uint32_t)it[4] >> (4 * nu) != 0u) fail("rotation bits past the units", round);
-    if (pairs_item > prev_pairs) fail("item order", round);
-    prev_pairs = pairs_item;
+    item_cost[i / 8] = pairs_item + 5 * nu;
+    /* a group of one unit (a single split, or one split of a long sequence) */
+    for (int u = 0; u < nu; ++u) {
+      const int b = (int)((uint32_t)it[u] & 0xFFFFFu);
+      const int s = (int)((uint32_t)it[u] >> 20);
+      const int64_t pages = (clamp_ctx64(ctx[b], stride) + 15) / 16;
+      const int64_t ns = pages == 0 ? 1 : (pages + sp - 1) / sp;
+      if (ns == 1 || ns > ucap) {
+        const int64_t pg = pages == 0 ? 0 : (pages - (int64_t)s * sp < sp ? pages - (int64_t)s * sp : sp);
+        if ((pg + 1) / 2 + 5 > max_group) max_group = (pg + 1) / 2 + 5;
+      }
+    }
   }
   if (placed != (num_seqs ? units : 0)) fail("units missing", round);
+  /* the bins' chains: every item once, forward, past the first items */
+  const int32_t slots = 256 / hkv > 0 ? 256 / hkv : 1;
+  const int32_t nb = nitems < slots ? nitems : slots;
+  char* reached = (char*)calloc((size_t)(nitems ? nitems : 1), 1);
+  if (!reached) fail("oom", round);
+  int64_t cmin = INT64_MAX, cmax = 0;
+  for (int32_t b = 0; b < nb; ++b) {
+    int64_t cost = 0;
+    for (int32_t k = b;;) {
+      if (reached[k]++) fail("item reached twice", round);
+      cost += item_cost[k];
+      const int32_t nxt = plan[(size_t)k * 8 + 5];
+      if (nxt == 0) break;
+      if (nxt <= k || nxt < nb || nxt >= nitems) fail("chain step", round);
+      k = nxt;
+    }
+    if (cost < cmin) cmin = cost;
+    if (cost > cmax) cmax = cost;
+  }
+  for (int32_t k = 0; k < nitems; ++k)
+    if (!reached[k]) fail("item not reached", round);
+  if (nb > 0 && cmax - cmin > max_group) fail("bin balance", round);
+  free(reached);
+  free(item_cost);
   free(seen);
   free(plan);
   free(ctx);

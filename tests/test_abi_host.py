@@ -166,55 +166,71 @@ def test_profile_and_status_strings():
 
 # ---- launch plan (pure host code)
 
-def expected_plan(ctx, stride, group=4, d=64, kv_heads=8, rounds_min=1):
+def expected_plan(ctx, stride, group=4, d=64, kv_heads=8):
     """The decode plan, restated: units are splits (2048 tokens at d = 64,
     1024 at d = 128); a sequence with at most ucap splits (4, or 2 when
     G > 8) is one group, a longer one a group per split, an empty context one
-    zero-pair unit. Groups by pairs (largest first, stable) go to the bin with
-    the fewest pairs (then the lowest index) that has room for their units,
-    among rounds x (256 / kv_heads) bins; a group no bin has room for opens a
-    new bin. Bins with units, by pairs (largest first, stable), become items of
-    8 words: units b | s << 20 (-1 for none), then the rotations (pairs before
-    the unit in its item, mod W, 4 bits per unit), then three zeros."""
+    zero-pair unit. A group costs its pairs plus 5 per unit. Groups by cost
+    (largest first, stable) go each to the bin of least cost so far (then the
+    lowest index), over min(groups, 256 / kv_heads) bins; in each bin, its
+    groups in that order go to the first of the bin's items with room for
+    their units, else to a new item. Bin b's first item is item b; the bins'
+    other items follow, bin by bin, each named by the item before it. An item
+    is 8 words: units b | s << 20 (-1 for none), the rotations (pairs before
+    the unit in its item, mod W, 4 bits per unit), the index of the bin's next
+    item (0: none), two zeros."""
+    import heapq
     sp, w = (128, 16) if d == 64 else (64, 8)
     ucap = 4 if group <= 8 else 2
-    groups = []          # (pairs, [(b, s, unit pairs)])
+    groups = []          # (cost, [(b, s, unit pairs)])
     for b, n in enumerate(ctx):
         n = min(max(int(n), 0), stride * 16)
         pages = (n + 15) // 16
         ns = (pages + sp - 1) // sp
         units = [(b, s, (min(pages - s * sp, sp) + 1) // 2) for s in range(ns)]
         if ns == 0:
-            groups.append((0, [(b, 0, 0)]))
+            groups.append((5, [(b, 0, 0)]))
         elif ns <= ucap:
-            groups.append((sum(u[2] for u in units), units))
+            groups.append((sum(u[2] for u in units) + 5 * ns, units))
         else:
-            groups.extend((u[2], [u]) for u in units)
-    total_units = sum(len(g[1]) for g in groups)
-    slots = max(1, 256 // kv_heads)
-    rounds = max(rounds_min, -(-total_units // (ucap * slots)))
-    nbins = min(len(groups), rounds * slots)
-    bins = [[0, []] for _ in range(nbins)]
-    for pairs, units in sorted(groups, key=lambda g: -g[0]):
-        room = [i for i, bn in enumerate(bins) if ucap - len(bn[1]) >= len(units)]
-        if room:
-            i = min(room, key=lambda i: (bins[i][0], i))
-        else:
-            bins.append([0, []])
-            i = len(bins) - 1
-        bins[i][0] += pairs
-        bins[i][1].extend(units)
-    out = []
-    for pairs, units in sorted([bn for bn in bins if bn[1]], key=lambda bn: -bn[0]):
-        words = [-1] * 4 + [0] * 4
-        before = rot = 0
-        for k, (b, s, p) in enumerate(units):
-            words[k] = b | (s << 20)
-            rot |= (before % w) << (4 * k)
-            before += p
-        words[4] = rot
-        out.extend(words)
-    return out
+            groups.extend((u[2] + 5, [u]) for u in units)
+    groups.sort(key=lambda g: -g[0])
+    nb = min(len(groups), max(1, 256 // kv_heads))
+    heap = [(0, i) for i in range(nb)]
+    bins = [[] for _ in range(nb)]
+    for cost, units in groups:
+        c, i = heapq.heappop(heap)
+        bins[i].append(units)
+        heapq.heappush(heap, (c + cost, i))
+    bin_items = []
+    for members in bins:
+        items = []
+        for units in members:
+            for it in items:
+                if len(it) + len(units) <= ucap:
+                    it.extend(units)
+                    break
+            else:
+                items.append(list(units))
+        bin_items.append(items)
+    out = [None] * sum(len(x) for x in bin_items)
+    extra = nb
+    for b, items in enumerate(bin_items):
+        idx = b
+        for k, units in enumerate(items):
+            nxt = 0
+            if k + 1 < len(items):
+                nxt, extra = extra, extra + 1
+            words = [-1] * 4 + [0] * 4
+            before = rot = 0
+            for j, (bb, s, p) in enumerate(units):
+                words[j] = bb | (s << 20)
+                rot |= (before % w) << (4 * j)
+                before += p
+            words[4], words[5] = rot, nxt
+            out[idx] = words
+            idx = nxt
+    return [x for words in out for x in words]
 
 
 def _plan_units(plan):
@@ -244,11 +260,26 @@ def test_plan_matches_its_statement_and_covers_every_unit():
             assert cap == len(ctx) * -(-stride // sp) * 8 and len(got) <= cap
             # every unit exactly once; short sequences whole and in split order
             seen = {}
-            for units, rot, zeros in _plan_units(got.tolist()):
-                assert 1 <= len(units) <= ucap and list(zeros) == [0, 0, 0]
+            items = _plan_units(got.tolist())
+            for units, rot, tail in items:
+                assert 1 <= len(units) <= ucap and list(tail[1:]) == [0, 0]
                 for k, (b, s) in enumerate(units):
                     assert (b, s) not in seen
                     seen[(b, s)] = (units, k)
+            # the chains from the bins' first items reach every item once,
+            # each step forward and past the first items
+            nb = min(len(items), 256 // hkv)
+            reached = []
+            for b in range(nb):
+                i = b
+                while True:
+                    reached.append(i)
+                    nxt = items[i][2][0]
+                    if nxt == 0:
+                        break
+                    assert i < nxt < len(items) and nxt >= nb
+                    i = nxt
+            assert sorted(reached) == list(range(len(items)))
             for b, n in enumerate(ctx):
                 n = min(max(int(n), 0), stride * 16)
                 ns = -(-((n + 15) // 16) // sp)

@@ -340,3 +340,47 @@ def test_planned_decode_is_bitwise_plain_decode(case):
         ref = oracle.decode_attention(up.q_host[0], w.pool_bits("k"), w.pool_bits("v"),
                                       w.block_tables[0], w.ctx_lens, w.scale)
         check_parity(out.cpu().numpy(), ref, "planned decode vs oracle")
+
+
+def test_plan_chains_guarded():
+    """A plan whose items chain behind the bins' first items (300 sequences of
+    at most 4 splits each, so every sequence is one item): with every chain
+    link broken (pointing back at its own item, or backwards, or past the
+    plan) each workgroup runs only its bin's first item and stops. The
+    sequences of the first items then match pa_decode bit for bit and every
+    other output row is left as it was (NaN)."""
+    import torch
+    dev = device()
+    rng = np.random.default_rng(404)
+    ctx = rng.integers(1, 4 * 2048 + 1, 300).astype(np.int32)
+    w = W.custom(seed=31, ctx_lens=ctx.tolist(), stride=512)
+    up = Uploaded(w, dev)
+    plain = up.step().clone()[0]
+    plan = B.decode_plan(up.pool, w.ctx_lens, w.num_q_heads, w.stride)
+    items = plan.reshape(-1, 8)
+    nb = min(len(items), 256 // w.num_kv_heads)
+    assert len(items) > nb, "the plan must chain items"
+    heads = set()
+    for i in range(nb):
+        heads.update(int(x) & 0xFFFFF for x in items[i, :4] if x >= 0)
+    for how in ("self", "back", "past"):
+        bad = items.copy()
+        idx = np.arange(len(items))
+        bad[:, 5] = {"self": idx, "back": np.maximum(idx - 1, 0), "past": len(items) + idx}[how]
+        log(f"broken chain links ({how}): {len(items)} items, {nb} bins")
+        for host in (False, True):
+            out = torch.full_like(plain, float("nan"))
+            if host:
+                B.decode_planned_host(up.pool, up.q[0], up.bt[0], up.ctx, float(w.scale), bad.reshape(-1),
+                                      out=out, workspace=up.workspace)
+            else:
+                B.decode_planned(up.pool, up.q[0], up.bt[0], up.ctx, float(w.scale),
+                                 torch.from_numpy(bad.reshape(-1).copy()).to(dev), out=out,
+                                 workspace=up.workspace)
+            torch.cuda.synchronize()
+            o, p = out.cpu().numpy(), plain.cpu().numpy()
+            for b in range(w.num_seqs):
+                if b in heads:
+                    assert np.array_equal(o[b], p[b]), f"{how}: sequence {b} of a first item"
+                else:
+                    assert np.isnan(o[b]).all(), f"{how}: sequence {b} written past a broken link"
