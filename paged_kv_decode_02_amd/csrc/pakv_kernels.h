@@ -402,6 +402,18 @@ __device__ __forceinline__ void stream_item(const StreamCtx<D>& c, int T, PairBu
   park_partial<D>(smem, cur * W + sel4(cur, lw0, lw1, lw2, lw3), G, st, r, grp);
 }
 
+// Max over lanes 0 .. N-1 of each row of 16 lanes (N = 8 or 16), in every
+// one of those lanes: DPP quad swaps, then the half-row and row mirrors.
+template <int N>
+__device__ __forceinline__ float row_max(float v) {
+  static_assert(N == 8 || N == 16, "row_max: 8 or 16 lanes");
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  if (N == 16) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -653,13 +665,14 @@ __device__ __forceinline__ int decode_item(const DecodeArgs& a, const InlinePlan
     any_whole = any_whole || ok;
   }
 
-  // merge each unit's W partials in logical-wave order
+  // merge each unit's W partials in logical-wave order: one wave per
+  // (unit, head) row, lane w reading logical wave w's max and sum, each lane
+  // its elements of the W partial accumulator rows
+  constexpr int PER = D / 64;
   const size_t head_kv = (size_t)kvh * G;
-  for (int e = tid; e < kItemUnits * G * D; e += 64 * W) {
-    const int u = e / (G * D);
-    const int rem = e - u * G * D;
-    const int hh = rem / D;
-    const int dd = rem - hh * D;
+  for (int row = wave; row < kItemUnits * G; row += W) {
+    const int u = row / G;
+    const int hh = row - u * G;
     const int b = sel4(u, ub[0], ub[1], ub[2], ub[3]);
     if (b < 0) continue;
     const int s = sel4(u, us[0], us[1], us[2], us[3]);
@@ -667,32 +680,49 @@ __device__ __forceinline__ int decode_item(const DecodeArgs& a, const InlinePlan
     const int ns = sel4(u, nsplit[0], nsplit[1], nsplit[2], nsplit[3]);
     const size_t head = (size_t)b * Hq + head_kv + hh;
     if (nn == 0) {
-      if (s == 0) a.out[head * D + dd] = 0.f;
+      if (s == 0) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) a.out[head * D + lane + 64 * i] = 0.f;
+      }
       continue;
     }
     if (s >= ns) continue;
-    float M = -INFINITY;
+    const float* pacc = smem + L::ACC + (size_t)(u * W * G + hh) * L::ROW + lane;
+    float x[W][PER];
 #pragma unroll
-    for (int w = 0; w < W; ++w) M = fmaxf(M, smem[L::WM + (u * W + w) * 16 + hh]);
-    float Ls = 0.f, A = 0.f;
+    for (int w = 0; w < W; ++w)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) x[w][i] = pacc[(size_t)w * G * L::ROW + 64 * i];
+    const float mv = lane < W ? smem[L::WM + (u * W + lane) * 16 + hh] : -INFINITY;
+    const float lv = lane < W ? smem[L::WL + (u * W + lane) * 16 + hh] : 0.f;
+    const float M = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(row_max<W>(mv))));
+    const float cw = __builtin_amdgcn_exp2f(mv - M);   // 0 in lanes >= W
+    float Ls = 0.f, A[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) A[i] = 0.f;
 #pragma unroll
     for (int w = 0; w < W; ++w) {
-      const float cw = __builtin_amdgcn_exp2f(smem[L::WM + (u * W + w) * 16 + hh] - M);
-      Ls += cw * smem[L::WL + (u * W + w) * 16 + hh];
-      A += cw * smem[L::ACC + (size_t)((u * W + w) * G + hh) * L::ROW + dd];
+      const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cw), w));
+      Ls += c * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), w));
+#pragma unroll
+      for (int i = 0; i < PER; ++i) A[i] += c * x[w][i];
     }
     if (ns == 1) {
-      a.out[head * D + dd] = A / Ls;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) a.out[head * D + lane + 64 * i] = A[i] / Ls;
     } else if (ns <= ucap) {
-      smem[L::ACC + (size_t)((u * W) * G + hh) * L::ROW + dd] = A;   // this thread's own element
-      if (dd == 0) {
+      // logical wave 0's row of this head (this wave's own) takes the unit's merged accumulator
+#pragma unroll
+      for (int i = 0; i < PER; ++i) smem[L::ACC + (size_t)((u * W) * G + hh) * L::ROW + lane + 64 * i] = A[i];
+      if (lane == 0) {
         smem[L::UM + u * 16 + hh] = M;
         smem[L::UL + u * 16 + hh] = Ls;
       }
     } else {
       const size_t slot = head * a.s_max + s;
-      a.ws_acc[slot * D + dd] = A;
-      if (dd == 0) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) a.ws_acc[slot * D + lane + 64 * i] = A[i];
+      if (lane == 0) {
         a.ws_ml[slot * 2] = M;
         a.ws_ml[slot * 2 + 1] = Ls;
       }
