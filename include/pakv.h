@@ -247,7 +247,11 @@ pa_status pa_decode_planned(const pa_pool* pool, const void* q, int32_t num_seqs
  * runtime copies when the launch is queued: nothing is copied to device
  * memory beforehand, no device plan buffer is needed, and plan_host may be
  * reused or freed as soon as the call returns. Larger plans give
- * PA_ERR_INVALID (use pa_decode_planned). Same results, bit for bit.
+ * PA_ERR_INVALID (use pa_decode_planned). Same results, bit for bit. The
+ * argument block grows with the plan (1 KiB up to 256 words, 8 KiB above):
+ * measured on MI355X, queueing an 8 KiB block costs the host ~60 us per
+ * launch against ~4 us for pa_decode_planned, whose plan is one copy to the
+ * device per step instead; the device time is the same either way.
  */
 pa_status pa_decode_planned_host(const pa_pool* pool, const void* q, int32_t num_seqs,
                                  int32_t num_q_heads, const int32_t* block_tables,

@@ -498,19 +498,31 @@ __device__ __forceinline__ int decode_item(const DecodeArgs& a, const InlinePlan
   int ub[kItemUnits], us[kItemUnits];
   int rot = 0;
   int next = -1;
+  int prefetched = 0;
   if (kInline || a.plan) {
     int it[kItemUnits + 2];
     if (kInline) {
 #pragma unroll
       for (int k = 0; k < kItemUnits + 2; ++k) it[k] = ip.w[item * kItemInts + k];
     } else {
+      // the plan does not change during a launch: scalar loads through the
+      // constant address space
+      typedef __attribute__((address_space(4))) const int32_t cint;
+      const cint* cplan = (const cint*)a.plan;
 #pragma unroll
-      for (int k = 0; k < kItemUnits + 2; ++k) it[k] = a.plan[(size_t)item * kItemInts + k];
+      for (int k = 0; k < kItemUnits + 2; ++k) it[k] = cplan[(size_t)item * kItemInts + k];
     }
     // every argument the next round of loads needs, in registers together
     asm volatile("" ::"s"(it[0]), "s"(it[1]), "s"(it[2]), "s"(it[3]), "s"(it[4]), "s"(it[5]), "s"(ctxp),
                  "s"(btp), "s"(qp), "s"(num_seqs), "s"(s_max), "s"(stride));
     next = it[kItemUnits + 1];
+    if constexpr (!kInline) {
+      // the chain's next record, touched now so that its load meets a warm
+      // scalar cache when this item is done (consumed below, at the end)
+      typedef __attribute__((address_space(4))) const int32_t cint;
+      const cint* cplan = (const cint*)a.plan;
+      prefetched = cplan[(size_t)min(max(next, 0), a.num_items - 1) * kItemInts];
+    }
 #pragma unroll
     for (int u = 0; u < kItemUnits; ++u) {
       const int e = it[u];
@@ -531,7 +543,10 @@ __device__ __forceinline__ int decode_item(const DecodeArgs& a, const InlinePlan
       us[u] = s;
     }
   }
-  if (ub[0] < 0 && ub[1] < 0 && ub[2] < 0 && ub[3] < 0) return next;
+  if (ub[0] < 0 && ub[1] < 0 && ub[2] < 0 && ub[3] < 0) {
+    asm volatile("" ::"s"(prefetched));
+    return next;
+  }
 
   // the second round, issued together and unconditionally (absent units read
   // sequence 0, whose row always exists, and are masked after): the context
@@ -728,7 +743,10 @@ __device__ __forceinline__ int decode_item(const DecodeArgs& a, const InlinePlan
       }
     }
   }
-  if (!any_whole) return next;
+  if (!any_whole) {
+    asm volatile("" ::"s"(prefetched));
+    return next;
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -743,6 +761,7 @@ __device__ __forceinline__ int decode_item(const DecodeArgs& a, const InlinePlan
       lse_merge<D>(nsplit[u0], lane, ml, acc, a.out + ((size_t)ub[u0] * Hq + head_kv + hh) * D);
     }
   }
+  asm volatile("" ::"s"(prefetched));
   return next;
 }
 
@@ -808,7 +827,9 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(DecodeArgs a) {
 // One 256-thread block per sequence: a bit copy of the new token's K row
 // (16-byte chunks, each to its slab of the K tile) and of its V values into
 // the slot-minor V layout, each V slot row (32 bytes) read, patched and
-// written whole.
+// written whole. Streaming (nontemporal) stores: the rows are read again
+// only by a later step, and lines left dirty in L2 would be written back at
+// the end of this launch, ahead of the decode that follows.
 template <int D>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   const int t = threadIdx.x;
@@ -825,8 +846,8 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   for (int c = t; c < H * (D / 8); c += 256) {
     const int g = c / (D / 8);
     const int part = c - g * (D / 8);
-    *(u32x4*)(a.kpool + (tile0 + g) * kPage * D + k_offset(slot, 8 * part)) =
-        *(const u32x4*)(kn + (size_t)g * D + 8 * part);
+    __builtin_nontemporal_store(*(const u32x4*)(kn + (size_t)g * D + 8 * part),
+                                (u32x4*)(a.kpool + (tile0 + g) * kPage * D + k_offset(slot, 8 * part)));
   }
   const int w = (slot & 7) >> 1;
   const int half = slot >> 3;
@@ -843,8 +864,8 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
       h0[i] = (half == 0 && i == w) ? upd0 : h0[i];
       h1[i] = (half == 1 && i == w) ? upd1 : h1[i];
     }
-    row[0] = h0;
-    row[1] = h1;
+    __builtin_nontemporal_store(h0, row);
+    __builtin_nontemporal_store(h1, row + 1);
   }
 }
 
