@@ -261,6 +261,23 @@ pa_status pa_decode_planned_host(const pa_pool* pool, const void* q, int32_t num
                                  int32_t num_ints, void* stream);
 
 /*
+ * pa_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments without the workspace, the same output bit for bit. The
+ * split partials go to the library's own scratch, a static device array of
+ * 32 MiB per device (held until the process ends; its address is looked up
+ * on the device's first call). Calls that would need more give
+ * PA_ERR_WORKSPACE (the need is pa_decode_workspace_bytes of the same
+ * sizes). Nothing is allocated or freed; the scratch needs no clearing
+ * (a launch reads only what it wrote). All calls on one GPU share that GPU's
+ * scratch: calls that overlap on one GPU (on different streams) race.
+ */
+pa_status pa_decode_static(const pa_pool* pool, const void* q, int32_t num_seqs,
+                           int32_t num_q_heads, const int32_t* block_tables,
+                           int32_t max_pages_per_seq, const int32_t* context_lens,
+                           float scale, float* out, void* stream);
+
+/*
  * Paged prefill. A chunk of new tokens per sequence: prefill fills a
  * request's pages (samir-vllm README review, KV-cache section) and processes
  * all of its tokens at once ("Construye tu propio motor de inferencia LLM

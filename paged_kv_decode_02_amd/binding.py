@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libpakv.so")
 
 PA_OK = 0
 PA_ERR_INVALID = 2
+PA_ERR_WORKSPACE = 5
 PA_ERR_CAPACITY = 7
 PA_ERR_STATE = 8
 STATUS_NAMES = {7: "PA_ERR_CAPACITY", 8: "PA_ERR_STATE",
@@ -30,7 +31,7 @@ EXPORTS = ["pa_pool_create", "pa_pool_destroy", "pa_kv_append", "pa_decode_works
            "pa_sched_submit_shared", "pa_sched_admit", "pa_sched_slot", "pa_sched_advance",
            "pa_sched_finish", "pa_sched_block_tables", "pa_sched_context_lens", "pa_sched_stats",
            "pa_kv_write", "pa_prefill", "pa_prefill_plan_capacity", "pa_prefill_plan",
-           "pa_prefill_planned", "pa_decode_planned_host"]
+           "pa_prefill_planned", "pa_decode_planned_host", "pa_decode_static"]
 
 _lib = None
 
@@ -88,6 +89,9 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_planned.restype = c.c_int
     L.pa_decode_planned_host.argtypes = list(L.pa_decode_planned.argtypes)
     L.pa_decode_planned_host.restype = c.c_int
+    L.pa_decode_static.argtypes = [c.c_void_p, c.c_void_p, c.c_int32, c.c_int32, c.c_void_p, c.c_int32,
+                                   c.c_void_p, c.c_float, c.c_void_p, c.c_void_p]
+    L.pa_decode_static.restype = c.c_int
     i32p, i64p = c.POINTER(c.c_int32), c.POINTER(c.c_int64)
     L.pa_sched_create.argtypes = [c.POINTER(c.c_void_p), c.c_int32, c.c_int32, c.c_int32, c.c_int32,
                                   c.c_int32]
@@ -286,6 +290,24 @@ def decode(pool: Pool, q, block_tables, context_lens, scale: float, out=None, wo
     _check(lib().pa_decode(pool.handle, _ptr(q), num_seqs, num_q_heads, _ptr(block_tables), stride,
                            _ptr(context_lens), float(scale), _ptr(out), _ptr(workspace), ws_bytes,
                            _stream(stream)), "pa_decode")
+    return out
+
+
+def decode_static(pool: Pool, q, block_tables, context_lens, scale: float, out=None, stream=None):
+    """pa_decode with the library's static scratch instead of a workspace
+    (pa_decode_static: nothing allocated on the device by the call)."""
+    import torch
+    _need(q, "q", _bf16_types(), 3)
+    _need(block_tables, "block_tables", (torch.int32,), 2)
+    _need(context_lens, "context_lens", (torch.int32,), 1)
+    _check_decode_args(pool, q, block_tables, context_lens, out)
+    num_seqs, num_q_heads, d = q.shape
+    if out is None:
+        out = torch.empty((num_seqs, num_q_heads, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,), 3)
+    _check(lib().pa_decode_static(pool.handle, _ptr(q), num_seqs, num_q_heads, _ptr(block_tables),
+                                  block_tables.shape[1], _ptr(context_lens), float(scale), _ptr(out),
+                                  _stream(stream)), "pa_decode_static")
     return out
 
 

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -23,6 +24,14 @@ struct pa_pool {
   int32_t num_kv_heads;
   int32_t head_dim;
 };
+
+// Scratch of the allocation-free decode (pa_decode_static): the split
+// partials (accumulators, then max and sum) of sequences with more splits
+// than one workgroup merges itself. Each device holds its own copy for the
+// life of the process. In host code this name stands for no device address:
+// the kernels get the address hipGetSymbolAddress gives on each device.
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -54,6 +63,23 @@ int prefill_wgs_per_cu(int d) {
 
 // decode workgroups one CU holds at once (waves per SIMD x 4 SIMDs / waves per workgroup)
 int decode_wgs_per_cu(int d) { return std::max(1, pakv::occupancy(d) * 4 / decode_waves(d)); }
+
+// The device address of the current device's scratch copy, looked up with
+// that device current on its first use and kept per device.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+pa_status static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_LAUNCH;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PA_ERR_LAUNCH;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return PA_OK;
+}
 
 // Workgroups per KV head that the device holds at once: the bins of a plan.
 int64_t decode_slots(const pa_pool* pool) {
@@ -517,6 +543,24 @@ pa_status pa_decode_planned_host(const pa_pool* pool, const void* q, int32_t num
   if (!plan_host && num_seqs > 0) return PA_ERR_NULL;
   return decode_impl(pool, q, num_seqs, num_q_heads, block_tables, max_pages_per_seq, context_lens, scale, out,
                      workspace, workspace_bytes, nullptr, plan_host, num_ints, stream);
+}
+
+pa_status pa_decode_static(const pa_pool* pool, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                           const int32_t* block_tables, int32_t max_pages_per_seq,
+                           const int32_t* context_lens, float scale, float* out, void* stream) {
+  if (!pool) return PA_ERR_NULL;
+  if (num_seqs < 0 || num_q_heads < 1 || max_pages_per_seq < 1) return PA_ERR_INVALID;
+  if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_INVALID;
+  if (num_seqs == 0) return PA_OK;
+  size_t acc_bytes = 0, need = 0;
+  workspace_parts(pool->head_dim, num_seqs, num_q_heads, num_q_heads / pool->num_kv_heads, max_pages_per_seq,
+                  &acc_bytes, &need);
+  if (need > kStaticScratchBytes) return PA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const pa_status st = static_scratch(&ws);
+  if (st != PA_OK) return st;
+  return decode_impl(pool, q, num_seqs, num_q_heads, block_tables, max_pages_per_seq, context_lens, scale, out,
+                     ws, kStaticScratchBytes, nullptr, nullptr, 0, stream);
 }
 
 pa_status pa_decode_append(const pa_pool* pool, const void* q, const void* k_new, const void* v_new,

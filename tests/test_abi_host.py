@@ -336,6 +336,23 @@ def test_plan_validation():
     L.pa_pool_destroy(h)
 
 
+def test_static_decode_validation():
+    """pa_decode_static checks its arguments and its scratch limit before it
+    touches a device: nothing here reaches the HIP runtime."""
+    L = B.lib()
+    h = make_pool(d=64)
+    f = L.pa_decode_static
+    assert f(None, P, 2, 32, P, 600, P, 0.125, P2, None) == NULL
+    assert f(h, P, -1, 32, P, 600, P, 0.125, P2, None) == INVALID
+    assert f(h, P, 2, 30, P, 600, P, 0.125, P2, None) == INVALID
+    assert f(h, P, 2, 32, P, 0, P, 0.125, P2, None) == INVALID
+    assert f(h, P, 0, 32, P, 600, P, 0.125, P2, None) == OK
+    # 600 sequences x 32 heads x 40 splits x (64 + 2) floats: past 32 MiB
+    assert L.pa_decode_workspace_bytes(h, 600, 32, 40 * 128) > 32 << 20
+    assert f(h, P, 600, 32, P, 40 * 128, P, 0.125, P2, None) == WORKSPACE
+    L.pa_pool_destroy(h)
+
+
 def test_planned_decode_validation():
     L = B.lib()
     h = make_pool(d=64)
