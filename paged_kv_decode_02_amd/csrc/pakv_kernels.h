@@ -149,8 +149,25 @@ struct AppendArgs {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ float xor_max(float v, int mask) {
-  return fmaxf(v, __shfl_xor(v, mask, 64));
+// Cross-lane steps with gfx950's permlane swaps (VALU, no LDS round trip):
+// a swap of a value with itself leaves, in every lane, the pair {own value,
+// value of lane ^ 16} (permlane16) or {own, lane ^ 32} (permlane32), in one
+// order or the other; max and sum of the pair are exact and order-free.
+__device__ __forceinline__ float pair_max16(float v) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float pair_max32(float v) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float pair_sum16(float v) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float pair_sum32(float v) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
 __device__ __forceinline__ int clamp_ctx(int n, int stride) {
@@ -269,8 +286,8 @@ __device__ __forceinline__ void compute_pair(const bf16x8 (&qf)[D / 32], float s
       sv[4 * j + i] = x;
       mx = fmaxf(mx, x);
     }
-  mx = xor_max(mx, 16);
-  mx = xor_max(mx, 32);
+  mx = pair_max16(mx);   // the 4 lanes of a head: r, r + 16, r + 32, r + 48
+  mx = pair_max32(mx);
   const float m_new = fmaxf(st.m, mx);
   const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
   float psum = 0.f;
@@ -333,8 +350,8 @@ template <int D>
 __device__ __forceinline__ void park_partial(float* smem, int slot, int G, const SoftmaxState<D>& st, int r,
                                              int grp) {
   using L = DecodeLds<D>;
-  float l = st.l + __shfl_xor(st.l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  float l = pair_sum16(st.l);
+  l = pair_sum32(l);
   if (grp == 0) {
     smem[L::WM + slot * 16 + r] = st.m;
     smem[L::WL + slot * 16 + r] = l;
