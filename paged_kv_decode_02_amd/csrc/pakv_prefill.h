@@ -191,12 +191,6 @@ __global__ __launch_bounds__(256) void kv_write_kernel(WriteArgs a) {
 }
 
 // -------------------------------------------------------------- attention
-template <int D>
-struct PrefillPair {
-  u32x4 k[2][D / 32];     // S^T A operands: MFMA j of the pair, k-step kk
-  u32x4 v[D / 16];        // O^T A operands: head-dim tile mt
-};
-
 template <int D, int RG>
 struct PrefillWave {
   const uint16_t* ktile;  // K pool + KV head tile of page 0
@@ -254,9 +248,12 @@ __device__ __forceinline__ float row_max4(float v) {
 constexpr float kLazyMax = 8.f;
 constexpr float kLazyBound = 256.f;   // 2^kLazyMax
 
+// The pair's scores and weights: S^T = K Q^T for every row group, then the
+// online softmax; ph / pl receive the weights' BF16 high and low parts.
 template <int D, int RG>
-__device__ __forceinline__ void prefill_compute(const PrefillWave<D, RG>& w, PrefillPair<D>& buf, int pr,
-                                                SoftmaxState<D> (&st)[RG], int grp) {
+__device__ __forceinline__ void prefill_softmax(const PrefillWave<D, RG>& w, const u32x4 (&kop)[2][D / 32], int pr,
+                                                SoftmaxState<D> (&st)[RG], int grp, bf16x8 (&ph)[RG],
+                                                bf16x8 (&pl)[RG]) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   constexpr int KK = D / 32;
@@ -265,7 +262,6 @@ __device__ __forceinline__ void prefill_compute(const PrefillWave<D, RG>& w, Pre
   const int key0 = 32 * pr + 8 * grp;
   // only a pair that some row of the wave cannot see whole needs the mask
   const bool diag = 32 * pr + 31 > w.first_pos;
-  bf16x8 ph[RG], pl[RG];
   // every row group's scores first, so that the matrix cores work on the
   // next group's while the VALU does this group's weights
   f32x4 scg[RG][2];
@@ -276,7 +272,7 @@ __device__ __forceinline__ void prefill_compute(const PrefillWave<D, RG>& w, Pre
       scg[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        scg[g][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf.k[j][kk]), w.qf[g][kk], scg[g][j], 0, 0, 0);
+        scg[g][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop[j][kk]), w.qf[g][kk], scg[g][j], 0, 0, 0);
     }
 #pragma unroll
   for (int g = 0; g < RG; ++g) {
@@ -338,6 +334,16 @@ __device__ __forceinline__ void prefill_compute(const PrefillWave<D, RG>& w, Pre
       pl[g][2 * q + 1] = lo[1];
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// O^T += V^T P^T for every row group, P as its BF16 high and low parts.
+template <int D, int RG>
+__device__ __forceinline__ void prefill_pv(const PrefillWave<D, RG>& w, u32x4 (&vop)[D / 16], int pr,
+                                           SoftmaxState<D> (&st)[RG], int grp, const bf16x8 (&ph)[RG],
+                                           const bf16x8 (&pl)[RG]) {
+  constexpr int MT = D / 16;
+  const int key0 = 32 * pr + 8 * grp;
   // keys past the wave's last position may be unwritten (NaN): zero their V
   // (dword q holds the lane's keys 2q, 2q+1: positions key0 + 2q, key0 + 2q + 1)
   if (32 * pr + 32 > w.last_pos + 1) {
@@ -350,14 +356,14 @@ __device__ __forceinline__ void prefill_compute(const PrefillWave<D, RG>& w, Pre
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) buf.v[mt][q] &= keep[q];
+      for (int q = 0; q < 4; ++q) vop[mt][q] &= keep[q];
   }
 #pragma unroll
   for (int g = 0; g < RG; ++g)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      st[g].acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf.v[mt]), ph[g], st[g].acc[mt], 0, 0, 0);
-      st[g].acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(buf.v[mt]), pl[g], st[g].acc[mt], 0, 0, 0);
+      st[g].acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vop[mt]), ph[g], st[g].acc[mt], 0, 0, 0);
+      st[g].acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vop[mt]), pl[g], st[g].acc[mt], 0, 0, 0);
     }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -388,22 +394,62 @@ __host__ __device__ constexpr int prefill_block_rows() { return 64 * prefill_row
 // longest blocks while others idle. With it, a CU's four blocks belong to
 // four sequences (8 sequences: offsets 0, 5, 2, 7). A launch plan made on
 // the host from the chunk and cache lengths (pa_prefill_plan) replaces this
-// order with one by work. Wave w of a block
-// takes rows w * 32 .. w * 32 + 31 in two groups of 16. The 4 waves share
-// every K/V tile: per page pair the workgroup loads K and V once (16-byte
-// loads, each thread its share), stores them to LDS in matrix-core operand
-// order (piece (MFMA j, k-step kk or dim tile mt, lane) at slot
-// (j KK + kk or mt) * 64 + lane, so both the stores and the waves' 16-byte
-// operand reads are lane-linear and free of bank conflicts), and every wave
-// reads its operands from there. Two LDS buffers: the next pair's
-// global loads are in flight while the current pair computes; one barrier
-// per pair.
+// order with one by work. Wave w of a block takes rows w * 32 .. w * 32 + 31
+// in two groups of 16.
+//
+// The 4 waves share every K/V tile through LDS. Per page pair the
+// workgroup copies K and V from the pages into LDS with direct-to-LDS
+// buffer loads (buffer_load_dwordx4 ... lds: 16 bytes per lane, written at
+// the wave's LDS base + 16 x lane, no registers on the way), in the order
+// the matrix cores read them. An operand area (K, or V) is 2 x 128
+// NPT 16-byte slots, the first half from the pair's first page, the second
+// from its second: slot t of a half holds, for K, piece (MFMA j, k-step kk
+// = block t / 32, lane group t % 32 / 8, key row t % 8 of the half's page)
+// and for V piece (dim tile t / 32, lane t % 32 of the half's page). A
+// wave's 64 slots therefore come from one page, so its load addresses are
+// that page's base (scalar) plus a fixed per-lane offset; a lane reading
+// its operand takes slot half x 128 NPT + block x 32 + (K) grp x 8 + r % 8
+// / (V) lane % 32: every run of 8 lanes reads 128 contiguous bytes, free of
+// bank conflicts. Four LDS buffers form a ring: pair p + 4's copies are
+// issued while pair p is computed, so three pairs' copies are in flight;
+// each wave waits for its own copies with vmcnt and one barrier per pair
+// makes all of them visible (and frees the buffer of the pair before).
 template <int D>
 struct PrefillLds {
   static constexpr int kKBytes = 2 * kPage * D * 2;     // K of a pair (two pages)
   static constexpr int kPairBytes = 2 * kKBytes;        // K and V
   static constexpr int kPerThread = (4 * D) / 256;      // 16-byte K (and V) pieces per thread
+  static constexpr int kHalfSlots = 128 * kPerThread;   // slots of one page in an operand area
 };
+// Fourth word of a raw buffer descriptor on gfx9: 32-bit data format, no
+// swizzle, no thread-id offsets (a zero data format would make loads return 0).
+constexpr int kBufferWord3 = 0x00020000;
+// Pairs whose copies are in the LDS ring at once (at d = 64 four
+// workgroups hold 4 x 32 KiB of a CU's 160 KiB; at d = 128, two hold 2 x 64 KiB).
+constexpr int kPrefillRing = 4;
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+// vmcnt bits 3:0, expcnt 6:4 = 7, lgkmcnt 11:8 = 15).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Waits until at most N of this wave's copies are in flight (the copies
+// issued after those of the pair about to be read), then a bare barrier:
+// every wave's copies of that pair have landed and every wave is done with
+// the buffer the next copy reuses (each wave's own LDS reads have returned:
+// lgkmcnt(0)). The empty asm statements keep the compiler from moving
+// memory accesses across it.
+template <int N>
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  wait_vm<N>();
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <int D>
 __global__ __launch_bounds__(256, prefill_occupancy<D>()) void prefill_kernel(PrefillArgs a) {
@@ -415,7 +461,11 @@ __global__ __launch_bounds__(256, prefill_occupancy<D>()) void prefill_kernel(Pr
   constexpr int NPT = PrefillLds<D>::kPerThread;
   constexpr int KB = PrefillLds<D>::kKBytes;
   constexpr int PB = PrefillLds<D>::kPairBytes;
-  __shared__ __attribute__((aligned(16))) char lds[2 * PB];
+  constexpr int HS = PrefillLds<D>::kHalfSlots;
+  static_assert(kPrefillRing == 4, "the loop below is unrolled for a ring of 4");
+  // separate arrays, indexed statically, so that the compiler can tell the
+  // ring's buffers apart and waits only for the copies a read needs
+  __shared__ __attribute__((aligned(16))) char ring0[PB], ring1[PB], ring2[PB], ring3[PB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -480,78 +530,136 @@ __global__ __launch_bounds__(256, prefill_occupancy<D>()) void prefill_kernel(Pr
                                                     : u32x4{0u, 0u, 0u, 0u});
   }
 
-  // this thread's 16-byte pieces of a pair: LDS slot tid + 256 i of the K
-  // (and of the V) operand area, so that the stores are lane-linear; the
-  // piece it loads is the one the matrix core wants there
-  uint32_t kg[NPT], vg[NPT], kl[NPT], vl[NPT];
-  bool kp2[NPT], vp2[NPT];
+  // this thread's copies of a pair: piece i fills slot tid + 256 i of the K
+  // (and of the V) area; the slot's half, hence the page, is the same for
+  // the whole wave
+  uint32_t kgo[NPT], vgo[NPT];   // byte offsets within the page's KV-head tile
+  bool second[NPT];
 #pragma unroll
   for (int i = 0; i < NPT; ++i) {
-    const int widx = tid + 256 * i;                    // operand slot: (MFMA / tile, lane)
-    const int ln = widx & 63;
-    const int lr = ln & 15;
-    const int lg = ln >> 4;
-    {  // K: MFMA j, k-step kk; QK row lr = page lr / 8, slot 8 ((lr / 4) % 2) + 4 j + lr % 4
-      const int jk = widx >> 6;
+    const int slot = tid + 256 * i;
+    const int t = slot % HS;
+    second[i] = slot >= HS;
+    {  // K: block (j, kk) = t / 32, lane group t % 32 / 8, key row t % 8 of the page
+      const int jk = t >> 5;
       const int j = jk / KK;
       const int kk = jk - j * KK;
-      const int slot = 8 * ((lr >> 2) & 1) + 4 * j + (lr & 3);
-      kg[i] = (uint32_t)k_offset(slot, kdim<D>(lg, kk));
-      kl[i] = (uint32_t)(widx * 16);
-      kp2[i] = (lr >> 3) != 0;
+      const int lg = (t >> 3) & 3;
+      const int lr = t & 7;                              // QK row lr (+ 8 on the second page)
+      const int key = 8 * ((lr >> 2) & 1) + 4 * j + (lr & 3);
+      kgo[i] = (uint32_t)(2 * k_offset(key, kdim<D>(lg, kk)));
     }
-    {  // V: head-dim tile mt; row 16 mt + lr, slots 8 (lg % 2) .. + 7 of page lg / 2
-      const int mt = widx >> 6;
-      vg[i] = (uint32_t)((16 * mt + lr) * kPage + 8 * (lg & 1));
-      vl[i] = (uint32_t)(KB + widx * 16);
-      vp2[i] = (lg >> 1) != 0;
+    {  // V: dim tile mt = t / 32, operand lane t % 32 (+ 32 on the second page)
+      const int mt = t >> 5;
+      const int ln = t & 31;
+      vgo[i] = (uint32_t)(2 * ((16 * mt + (ln & 15)) * kPage + 8 * (ln >> 4)));
     }
   }
-  u32x4 sk[NPT], sv[NPT];
-  auto gload = [&](int pr) {
-    int pa, pb;
+  // LDS byte offsets of this lane's operands in a buffer
+  const uint32_t kread = (uint32_t)(16 * ((r >> 3) * HS + grp * 8 + (r & 7)));
+  const uint32_t vread = (uint32_t)(KB + 16 * ((grp >> 1) * HS + (lane & 31)));
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  constexpr int kTileBytes = kPage * D * 2;        // one page's K (or V) of one KV head
+  // The pair's copies into buffer `dst`, from pages pa and pb. They are
+  // buffer loads with the LDS destination (buffer_load_dwordx4 ... lds):
+  // with them the compiler still waits for LDS reads one by one (lgkmcnt
+  // n), which it does not after the flat-encoded global-to-LDS form. Every step
+  // issues one pair's copies, also past the last pair (then the last pair's
+  // pages again, which no one reads), so that the wait before each pair is
+  // the same count. The page half of piece i is the same for the whole wave.
+  auto copy_pair = [&](int pa, int pb, char* dst) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int pid = (64 * wave + 256 * i) >= HS ? pb : pa;
+      // buffer descriptors of the page's K and V tiles of this KV head
+      // (offsets checked against the tile's bytes)
+      const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(w.ktile + (size_t)pid * w.page_elems), (short)0, kTileBytes, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(w.vtile + (size_t)pid * w.page_elems), (short)0, kTileBytes, kBufferWord3);
+      char* wbase = dst + 16 * (64 * wave + 256 * i);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_ptr)wbase, 16, (int)kgo[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_ptr)(wbase + KB), 16, (int)vgo[i], 0, 0, 0);
+    }
+  };
+  // page ids of pair pr (clamped to the block's last pair)
+  auto pages_of = [&](int pr, int& pa, int& pb) {
+    pr = min(pr, npairs - 1);
     pair_pages(w, 2 * pr, min(2 * pr + 1, blk_pages - 1), pa, pb);
-    const uint16_t* ka = w.ktile + (size_t)pa * w.page_elems;
-    const uint16_t* kb = w.ktile + (size_t)pb * w.page_elems;
-    const uint16_t* va = w.vtile + (size_t)pa * w.page_elems;
-    const uint16_t* vb = w.vtile + (size_t)pb * w.page_elems;
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      sk[i] = *(const u32x4*)((kp2[i] ? kb : ka) + kg[i]);
-      sv[i] = *(const u32x4*)((vp2[i] ? vb : va) + vg[i]);
-    }
   };
-  auto lstore = [&](int bufi) {
-    char* base = lds + bufi * PB;
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      *(u32x4*)(base + kl[i]) = sk[i];
-      *(u32x4*)(base + vl[i]) = sv[i];
-    }
-  };
-
   SoftmaxState<D> st[RG];
 #pragma unroll
   for (int g = 0; g < RG; ++g) init_state(st[g]);
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int pr = 0; pr < npairs; ++pr) {
-    if (pr + 1 < npairs) gload(pr + 1);
-    if (active && 32 * pr <= w.last_pos) {
-      const char* base = lds + (pr & 1) * PB;
-      PrefillPair<D> buf;
+  // this lane's operands of the pair being computed: K for the scores, V
+  // for the weighted sum; each is read from LDS one phase before its use
+  u32x4 kop[2][KK], vop[MT];
+  auto read_k = [&](const char* buf) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) buf.k[j][kk] = *(const u32x4*)(base + ((j * KK + kk) * 64 + lane) * 16);
+      for (int kk = 0; kk < KK; ++kk) kop[j][kk] = *(const u32x4*)(buf + kread + 512 * (j * KK + kk));
+  };
+  auto read_v = [&](const char* buf) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) buf.v[mt] = *(const u32x4*)(base + KB + (mt * 64 + lane) * 16);
-      prefill_compute(w, buf, pr, st, grp);
+    for (int mt = 0; mt < MT; ++mt) vop[mt] = *(const u32x4*)(buf + vread + 512 * mt);
+  };
+  // page ids of the pair a copy is for, read right before the barrier that
+  // precedes the copy, whose wait (lgkmcnt(0)) covers their scalar loads
+  int pa, pb;
+  // the first four pairs' copies fill the ring; pair p lives in buffer p % 4
+  constexpr int NL = 2 * NPT;   // copies per pair and thread
+  pages_of(0, pa, pb);
+  copy_pair(pa, pb, ring0);
+  pages_of(1, pa, pb);
+  copy_pair(pa, pb, ring1);
+  pages_of(2, pa, pb);
+  copy_pair(pa, pb, ring2);
+  pages_of(3, pa, pb);
+  copy_pair(pa, pb, ring3);
+  ring_barrier<3 * NL>();   // pair 0 (pairs 1-3 may be in flight)
+  read_k(ring0);
+  read_v(ring0);
+  // One step computes pair pr (its K and V already in registers): the
+  // scores and weights; the barrier for pair pr + 1 (its copies have
+  // landed, and every wave is done with pair pr's buffer); the copy of
+  // pair pr + 4 into that buffer; the read of pair pr + 1's K, then the
+  // weighted sum of pair pr, then the read of pair pr + 1's V. Every LDS
+  // read thus has a phase of matrix-core work to land in.
+  auto step = [&](int pr, char* cur, const char* nxt, bool issue) {
+    const bool doit = active && 32 * pr <= w.last_pos;
+    bf16x8 ph[RG], pl[RG];
+    if (doit) prefill_softmax(w, kop, pr, st, grp, ph, pl);
+    if (issue) {
+      pages_of(pr + 4, pa, pb);
+      ring_barrier<2 * NL>();   // pair pr + 1 (pairs pr + 2, pr + 3 may be in flight)
+      copy_pair(pa, pb, cur);
+    } else {
+      // the last pairs: every copy was issued already; wait for all of them
+      asm volatile("" ::: "memory");
+      wait_vm<0>();
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     }
-    if (pr + 1 < npairs) lstore((pr + 1) & 1);
-    __syncthreads();
+    read_k(nxt);
+    if (doit) prefill_pv(w, vop, pr, st, grp, ph, pl);
+    read_v(nxt);
+  };
+  // whole rounds of four pairs (a loop without early exits, so that the
+  // compiler's own wait analysis sees the ring's buffers apart), then the
+  // last 0-3 pairs, which issue no copies
+  int pr = 0;
+  for (; pr + 4 <= npairs; pr += 4) {
+    step(pr, ring0, ring1, true);
+    step(pr + 1, ring1, ring2, true);
+    step(pr + 2, ring2, ring3, true);
+    step(pr + 3, ring3, ring0, true);
   }
+  if (pr < npairs) step(pr, ring0, ring1, false);
+  if (pr + 1 < npairs) step(pr + 1, ring1, ring2, false);
+  if (pr + 2 < npairs) step(pr + 2, ring2, ring3, false);
+  // no copy may still be writing this workgroup's LDS when it ends
+  wait_vm<0>();
 #pragma unroll
   for (int g = 0; g < RG; ++g) {
     float l = st[g].l;
