@@ -194,18 +194,26 @@ pa_status pa_decode_append(const pa_pool* pool, const void* q, const void* k_new
  * Launch plan (host side, optional). Without one, pa_decode runs one
  * workgroup per sequence and group of splits, however uneven the contexts.
  * A plan packs the batch's units (one split of one sequence each) into work
- * items of up to 4 units (2 when more than 8 query heads share a KV head),
- * one workgroup per item and KV head, so that the workgroups carry even
- * work: a sequence with at most that many splits stays whole in one item
- * (finished inside its workgroup, as without a plan); the splits of a longer
- * one are placed one by one. Units go largest first to the item with the
- * fewest page pairs that has room, over one round of the device (256 CUs,
- * one decode workgroup each) times the rounds the unit count needs; items
- * are listed by pairs, largest first. Each item also carries, per unit, the
- * count of pairs before it (mod the waves per workgroup), so the
- * workgroup's waves deal all of the item's pairs round-robin. Serving code
- * knows its context lengths on the host, and one plan serves every layer of
- * a step.
+ * items of up to 4 units (2 when more than 8 query heads share a KV head)
+ * and the items into bins, one persistent workgroup per bin and KV head
+ * that runs its bin's items in turn:
+ *  - a sequence with at most that many splits is one group, kept whole in
+ *    one item (finished inside its workgroup, as without a plan); a longer
+ *    one gives one group per split (its split partials merged by the merge
+ *    kernel);
+ *  - a group costs its page pairs plus 5 per unit (the fixed work of an
+ *    item's start and merge); groups, costliest first, go each to the bin
+ *    of least cost so far (ties: the lower bin), over as many bins as the
+ *    device holds decode workgroups at once divided by the KV heads (or one
+ *    per group when there are fewer groups), so that the bins end together;
+ *  - in each bin, its groups in that order go to the first of its items
+ *    with room (a new item when none has);
+ *  - item b (b < bins) is bin b's first item; every item names the bin's
+ *    next one, and those are listed after all the first items, bin by bin.
+ * Each item also carries, per unit, the count of pairs before it in the
+ * item (mod the waves per workgroup), so the workgroup's waves deal all of
+ * the item's pairs round-robin. Serving code knows its context lengths on
+ * the host, and one plan serves every layer of a step.
  *
  * pa_decode_plan_capacity: int32 words a plan may need for these sizes
  * (8 per possible unit: num_seqs * splits per sequence * 8), or -1 when the
@@ -216,7 +224,11 @@ pa_status pa_decode_append(const pa_pool* pool, const void* q, const void* k_new
  * kernel does) and num_q_heads into plan[capacity] (host memory) and its
  * length in int32 words into *num_ints. Item encoding, 8 words: units
  * b | (split << 20), or -1 for none, in words 0..3; the units' rotations,
- * 4 bits each, in word 4; words 5..7 zero. Pure host code; queues nothing.
+ * 4 bits each, in word 4; the index of the bin's next item in word 5 (0 for
+ * none; the kernel ends a chain at any index that is not above the
+ * current one or not among the items after the first ones); words 6..7
+ * zero. Pure host code; queues nothing. PA_ERR_INVALID when the plan would
+ * not fit `capacity` or host memory runs out.
  */
 int64_t pa_decode_plan_capacity(const pa_pool* pool, int32_t num_seqs,
                                 int32_t max_pages_per_seq);

@@ -184,8 +184,8 @@ template <int D>
 __host__ __device__ constexpr bool nt_v() { return true; }
 
 // Head dims held by lane group grp for QK k-step kk (8 consecutive dims):
-// k-step kk covers K slab kk. The keys (A operand), the query (B operand),
-// the fused append and the prefill use it.
+// k-step kk covers K slab kk. The keys (A operand), the query (B operand)
+// and the prefill use it.
 template <int D>
 __host__ __device__ constexpr int kdim(int grp, int kk) { return 8 * grp + 32 * kk; }
 
