@@ -171,8 +171,13 @@ pa_status launch_decode_with(const pakv::DecodeArgs& args, const pakv::InlinePla
     pakv::DecodeArgs a = args;
     a.num_items = static_cast<int32_t>(items);
     a.num_bins = static_cast<int32_t>(bins);
-    hipLaunchKernelGGL((pakv::decode_kernel<D, NW>), dim3(static_cast<unsigned>(args.num_kv_heads), gy, gz),
-                       dim3(64 * pakv::DecodeGeom<D>::W), 0, stream, a, ip);
+    // a chain can only reach items past the bins' first ones
+    if (items > bins)
+      hipLaunchKernelGGL((pakv::decode_kernel<D, NW, true>), dim3(static_cast<unsigned>(args.num_kv_heads), gy, gz),
+                         dim3(64 * pakv::DecodeGeom<D>::W), 0, stream, a, ip);
+    else
+      hipLaunchKernelGGL((pakv::decode_kernel<D, NW, false>), dim3(static_cast<unsigned>(args.num_kv_heads), gy, gz),
+                         dim3(64 * pakv::DecodeGeom<D>::W), 0, stream, a, ip);
   }
   if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
   if (args.s_max > args.ucap) {

@@ -786,8 +786,11 @@ __device__ __forceinline__ int decode_item(const DecodeArgs& a, const InlinePlan
 // items need no barrier between them: an item writes the query rows (read
 // only while streaming, which ended at the previous item's merge barrier)
 // before its first barrier, and the partials only after it, when every wave
-// has finished the previous item's merge.
-template <int D, int NW>
+// has finished the previous item's merge. CHAIN = false is the form for
+// launches in which no item can be chained (no more items than bins): each
+// workgroup runs its one item, without the loop, which measured ~0.5 us
+// faster on such one-round launches (64 sequences of up to 2048 tokens).
+template <int D, int NW, bool CHAIN>
 __global__ __launch_bounds__(64 * DecodeGeom<D>::W, occupancy(D)) void decode_kernel(DecodeArgs a,
                                                                                    InlinePlan<NW> ip) {
   static_assert(D == 64 || D == 128, "head_dim");
@@ -806,18 +809,22 @@ __global__ __launch_bounds__(64 * DecodeGeom<D>::W, occupancy(D)) void decode_ke
   if constexpr (!kInline) {
     if (bin >= a.num_bins) return;
   }
-  int item = bin;
-  for (;;) {
-    // each item derives its per-lane values afresh (opaque copies of the
-    // thread and KV head indices): none is held in registers across items
-    int h = kvh;
-    int tid = threadIdx.x;
-    asm volatile("" : "+s"(h), "+v"(tid));
-    const int next = decode_item<D, NW>(a, ip, h, tid, item, smem);
-    // a chain only moves forward, past the bins' first items and inside the
-    // plan: it ends after at most num_items items whatever the plan holds
-    if (next <= item || next < a.num_bins || next >= a.num_items) break;
-    item = next;
+  if constexpr (!CHAIN) {
+    decode_item<D, NW>(a, ip, kvh, threadIdx.x, bin, smem);
+  } else {
+    int item = bin;
+    for (;;) {
+      // each item derives its per-lane values afresh (opaque copies of the
+      // thread and KV head indices): none is held in registers across items
+      int h = kvh;
+      int tid = threadIdx.x;
+      asm volatile("" : "+s"(h), "+v"(tid));
+      const int next = decode_item<D, NW>(a, ip, h, tid, item, smem);
+      // a chain only moves forward, past the bins' first items and inside
+      // the plan: it ends after at most num_items items whatever the plan holds
+      if (next <= item || next < a.num_bins || next >= a.num_items) break;
+      item = next;
+    }
   }
 }
 
