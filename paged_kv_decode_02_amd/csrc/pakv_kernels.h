@@ -851,45 +851,100 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(DecodeArgs a) {
 // One 256-thread block per sequence: a bit copy of the new token's K row
 // (16-byte chunks, each to its slab of the K tile) and of its V values into
 // the slot-minor V layout, each V slot row (32 bytes) read, patched and
-// written whole. Streaming (nontemporal) stores: the rows are read again
-// only by a later step, and lines left dirty in L2 would be written back at
-// the end of this launch, ahead of the decode that follows.
+// written whole. The new token's values do not depend on where it goes, so
+// they are loaded first, in flight while the position and the block-table
+// entry are read; the V rows it patches are then all loaded together. The
+// block's first kAppendK chunks and kAppendV values are held this way (all
+// of them for up to 8 KV heads of 64 dims); larger shapes loop over the
+// rest. Streaming (nontemporal) stores: the rows are read again only by a
+// later step, and lines left dirty in L2 would be written back at the end
+// of this launch, ahead of the decode that follows.
+constexpr int kAppendK = 1;   // 16-byte K chunks per thread held in registers
+constexpr int kAppendV = 2;   // V values (and their slot rows) per thread held in registers
+
+template <int D>
+__device__ __forceinline__ u32x4 patch_slot(u32x4 h, int half, int q, int w, uint32_t sh, uint32_t nv) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t upd = (h[i] & ~(0xFFFFu << sh)) | (nv << sh);
+    h[i] = (half == q && i == w) ? upd : h[i];
+  }
+  return h;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   const int t = threadIdx.x;
   const int b = blockIdx.x;
+  const int H = a.num_kv_heads;
+  const uint16_t* kn = a.k_new + (size_t)b * H * D;
+  const uint16_t* vn = a.v_new + (size_t)b * H * D;
+  const int kchunks = H * (D / 8);
+  const int vvals = H * D;
+  u32x4 kv[kAppendK];
+  uint32_t vv[kAppendV];
+#pragma unroll
+  for (int i = 0; i < kAppendK; ++i) {
+    const int c = t + 256 * i;
+    kv[i] = c < kchunks ? *(const u32x4*)(kn + 8 * (size_t)c) : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int i = 0; i < kAppendV; ++i) {
+    const int e = t + 256 * i;
+    vv[i] = e < vvals ? (uint32_t)vn[e] : 0u;
+  }
   const int pos = a.positions[b];
   if (pos < 0 || pos >= a.stride * kPage) return;
   const int pid = a.block_tables[(size_t)b * a.stride + pos / kPage];
   if (pid < 0 || pid >= a.num_pages) return;
   const int slot = pos % kPage;
-  const int H = a.num_kv_heads;
   const size_t tile0 = (size_t)pid * H;
-  const uint16_t* kn = a.k_new + (size_t)b * H * D;
-  const uint16_t* vn = a.v_new + (size_t)b * H * D;
-  for (int c = t; c < H * (D / 8); c += 256) {
-    const int g = c / (D / 8);
-    const int part = c - g * (D / 8);
-    __builtin_nontemporal_store(*(const u32x4*)(kn + (size_t)g * D + 8 * part),
-                                (u32x4*)(a.kpool + (tile0 + g) * kPage * D + k_offset(slot, 8 * part)));
-  }
   const int w = (slot & 7) >> 1;
   const int half = slot >> 3;
   const uint32_t sh = (slot & 1) * 16;
-  for (int e = t; e < H * D; e += 256) {     // row e = (kv head, dim)
-    u32x4* row = (u32x4*)(a.vpool + (tile0 * D + e) * kPage);
-    u32x4 h0 = row[0];
-    u32x4 h1 = row[1];
-    const uint32_t nv = vn[e];
+  // the V slot rows of the held values, loaded together
+  u32x4 h0[kAppendV], h1[kAppendV];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t upd0 = (h0[i] & ~(0xFFFFu << sh)) | (nv << sh);
-      const uint32_t upd1 = (h1[i] & ~(0xFFFFu << sh)) | (nv << sh);
-      h0[i] = (half == 0 && i == w) ? upd0 : h0[i];
-      h1[i] = (half == 1 && i == w) ? upd1 : h1[i];
+  for (int i = 0; i < kAppendV; ++i) {
+    const int e = t + 256 * i;   // row e = (kv head, dim)
+    if (e < vvals) {
+      const u32x4* row = (const u32x4*)(a.vpool + (tile0 * D + e) * kPage);
+      h0[i] = row[0];
+      h1[i] = row[1];
     }
-    __builtin_nontemporal_store(h0, row);
-    __builtin_nontemporal_store(h1, row + 1);
+  }
+#pragma unroll
+  for (int i = 0; i < kAppendK; ++i) {
+    const int c = t + 256 * i;
+    if (c < kchunks) {
+      const int g = c / (D / 8);
+      const int part = c - g * (D / 8);
+      __builtin_nontemporal_store(kv[i], (u32x4*)(a.kpool + (tile0 + g) * kPage * D + k_offset(slot, 8 * part)));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kAppendV; ++i) {
+    const int e = t + 256 * i;
+    if (e < vvals) {
+      u32x4* row = (u32x4*)(a.vpool + (tile0 * D + e) * kPage);
+      __builtin_nontemporal_store(patch_slot<D>(h0[i], half, 0, w, sh, vv[i]), row);
+      __builtin_nontemporal_store(patch_slot<D>(h1[i], half, 1, w, sh, vv[i]), row + 1);
+    }
+  }
+  // shapes beyond what the registers hold
+  for (int c = t + 256 * kAppendK; c < kchunks; c += 256) {
+    const int g = c / (D / 8);
+    const int part = c - g * (D / 8);
+    __builtin_nontemporal_store(*(const u32x4*)(kn + 8 * (size_t)c),
+                                (u32x4*)(a.kpool + (tile0 + g) * kPage * D + k_offset(slot, 8 * part)));
+  }
+  for (int e = t + 256 * kAppendV; e < vvals; e += 256) {
+    u32x4* row = (u32x4*)(a.vpool + (tile0 * D + e) * kPage);
+    const uint32_t nv = vn[e];
+    const u32x4 r0 = row[0];
+    const u32x4 r1 = row[1];
+    __builtin_nontemporal_store(patch_slot<D>(r0, half, 0, w, sh, nv), row);
+    __builtin_nontemporal_store(patch_slot<D>(r1, half, 1, w, sh, nv), row + 1);
   }
 }
 
