@@ -201,7 +201,7 @@ pa_status pa_decode_append(const pa_pool* pool, const void* q, const void* k_new
  *    one item (finished inside its workgroup, as without a plan); a longer
  *    one gives one group per split (its split partials merged by the merge
  *    kernel);
- *  - a group costs its page pairs plus 5 per unit (the fixed work of an
+ *  - a group costs its page pairs plus 2 per unit (the fixed work of an
  *    item's start and merge); groups, costliest first, go each to the bin
  *    of least cost so far (ties: the lower bin), over as many bins as the
  *    device holds decode workgroups at once divided by the KV heads (or one

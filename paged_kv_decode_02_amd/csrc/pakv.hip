@@ -416,7 +416,8 @@ pa_status pa_decode_plan(const pa_pool* pool, const int32_t* context_lens_host, 
 //    are merged inside the workgroup); a longer one gives one group per
 //    split (merged by the merge kernel);
 //  - a group costs its pairs plus kUnitCost per unit (an item's fixed work,
-//    the start of its stream and its merge, shared by its units); groups go,
+//    the start of its stream and its merge, shared by its units; 2 measured
+//    a little faster than 0, 5, 10 or 20 on the 16-layer step); groups go,
 //    costliest first, each to the bin of least cost so far, over as many
 //    bins as the device holds workgroups at once (or one per group, if there
 //    are fewer groups), so that the bins end together;
@@ -426,7 +427,7 @@ pa_status pa_decode_plan(const pa_pool* pool, const int32_t* context_lens_host, 
 //    one, listed after all the first items.
 // A unit's rotation is the number of pairs before it in its item, mod W:
 // the workgroup's waves then deal all of the item's pairs round-robin.
-constexpr int64_t kUnitCost = 5;
+constexpr int64_t kUnitCost = 2;
 
 static pa_status decode_plan_impl(const pa_pool* pool, const int32_t* context_lens_host, int32_t num_seqs,
                                   int group, int32_t max_pages_per_seq, int32_t* plan, int64_t capacity,

@@ -9,7 +9,7 @@
  *     item; each unit's rotation the pairs before it in its item mod the
  *     workgroup's waves; the bins' chains (item b < bins first, each item
  *     naming the next) reach every item once, moving forward past the first
- *     items; bin costs (pairs + 5 per unit) within one group's cost of each
+ *     items; bin costs (pairs + 2 per unit) within one group's cost of each
  *     other; and the same call into a buffer one word short of the plan
  *     refused, nothing written past it;
  *   - pa_prefill_plan on random cache and chunk lengths (negative and past
@@ -134,7 +134,7 @@ static void plan_round(long round) {
           const int64_t pv = pages - v * sp < sp ? pages - v * sp : sp;
           gp += (pv + 1) / 2;
         }
-        if (gp + 5 * ns > max_group) max_group = gp + 5 * ns;
+        if (gp + 2 * ns > max_group) max_group = gp + 2 * ns;
         if (u + ns > 4) fail("short sequence cut", round);
         for (int v = 1; v < ns; ++v)
           if (it[u + v] != (int32_t)((uint32_t)b | ((uint32_t)v << 20))) fail("short sequence cut", round);
@@ -144,7 +144,7 @@ static void plan_round(long round) {
     }
     if (nu == 0 || nu > ucap) fail("units per item", round);
     if ((uint32_t)it[4] >> (4 * nu) != 0u) fail("rotation bits past the units", round);
-    item_cost[i / 8] = pairs_item + 5 * nu;
+    item_cost[i / 8] = pairs_item + 2 * nu;
     /* a group of one unit (a single split, or one split of a long sequence) */
     for (int u = 0; u < nu; ++u) {
       const int b = (int)((uint32_t)it[u] & 0xFFFFFu);
@@ -153,7 +153,7 @@ static void plan_round(long round) {
       const int64_t ns = pages == 0 ? 1 : (pages + sp - 1) / sp;
       if (ns == 1 || ns > ucap) {
         const int64_t pg = pages == 0 ? 0 : (pages - (int64_t)s * sp < sp ? pages - (int64_t)s * sp : sp);
-        if ((pg + 1) / 2 + 5 > max_group) max_group = (pg + 1) / 2 + 5;
+        if ((pg + 1) / 2 + 2 > max_group) max_group = (pg + 1) / 2 + 2;
       }
     }
   }

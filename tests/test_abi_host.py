@@ -170,7 +170,7 @@ def expected_plan(ctx, stride, group=4, d=64, kv_heads=8):
     """The decode plan, restated: units are splits (2048 tokens at d = 64,
     1024 at d = 128); a sequence with at most ucap splits (4, or 2 when
     G > 8) is one group, a longer one a group per split, an empty context one
-    zero-pair unit. A group costs its pairs plus 5 per unit. Groups by cost
+    zero-pair unit. A group costs its pairs plus 2 per unit. Groups by cost
     (largest first, stable) go each to the bin of least cost so far (then the
     lowest index), over min(groups, 256 / kv_heads) bins; in each bin, its
     groups in that order go to the first of the bin's items with room for
@@ -189,11 +189,11 @@ def expected_plan(ctx, stride, group=4, d=64, kv_heads=8):
         ns = (pages + sp - 1) // sp
         units = [(b, s, (min(pages - s * sp, sp) + 1) // 2) for s in range(ns)]
         if ns == 0:
-            groups.append((5, [(b, 0, 0)]))
+            groups.append((2, [(b, 0, 0)]))
         elif ns <= ucap:
-            groups.append((sum(u[2] for u in units) + 5 * ns, units))
+            groups.append((sum(u[2] for u in units) + 2 * ns, units))
         else:
-            groups.extend((u[2] + 5, [u]) for u in units)
+            groups.extend((u[2] + 2, [u]) for u in units)
     groups.sort(key=lambda g: -g[0])
     nb = min(len(groups), max(1, 256 // kv_heads))
     heap = [(0, i) for i in range(nb)]
